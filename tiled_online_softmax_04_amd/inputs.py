@@ -1,0 +1,250 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the tests, the benchmark and the oracle checks.  It
+draws random numbers and rounds them to the storage dtypes; it contains none
+of the attention arithmetic (no scores, no softmax, no weighted sums).
+
+Recipe (every workload):
+  * generator: ``numpy.random.default_rng(seed)`` (PCG64);
+  * draws, in this order: Q, K, V as float32 standard normals, then the
+    ragged lengths / sequence lengths (integers, inclusive bounds), then the
+    physical block permutation of a paged cache;
+  * "hot" data multiplies Q and K by 10 in float32 before the cast (the
+    overflow experiment of the 10100.com article, section 4);
+  * storage casts are round-to-nearest-even: float32 -> bfloat16 by bit
+    arithmetic, float32 -> float16 by numpy's cast.
+Padding rows of a left-padded batch, cache slots past a sequence's length and
+unused block-table columns hold poison (NaN / -1) so that a kernel that reads
+them is caught.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# --------------------------------------------------------------------------
+# dtype rounding (storage formats only)
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16, nearest-even, returned as uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def store(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> the storage array for ``dtype`` (bf16 as uint16 bits)."""
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(x32.astype(np.float16))
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    raise ValueError(dtype)
+
+
+def to_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 upcast of a storage array."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(stored)
+    return np.asarray(stored).astype(np.float64)
+
+
+def poison_value(dtype: str):
+    if dtype == "bf16":
+        return BF16_NAN
+    return np.nan
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    n: int
+    m: int
+    d: int
+    dv: int
+    causal: bool
+    seed: int
+    hot: float = 1.0          # factor applied to Q and K
+    ragged: tuple | None = None  # (lo, hi) inclusive bounds of left-padded lengths
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    name: str
+    dtype: str
+    num_seqs: int
+    Hq: int
+    Hkv: int
+    d: int
+    dv: int
+    block_size: int
+    len_lo: int
+    len_hi: int
+    max_blocks_per_seq: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The five workloads (sizes as the benchmark spec gives them).
+WORKLOADS = {
+    "cfg1": Prefill("cfg1", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1),
+    "cfg1_hot": Prefill("cfg1_hot", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1, hot=10.0),
+    "cfg2": Prefill("cfg2", "bf16", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
+    "cfg3": Prefill("cfg3", "bf16", 1, 32, 32, 8192, 8192, 128, 128, True, seed=3),
+    "cfg3_ragged": Prefill("cfg3_ragged", "bf16", 8, 32, 32, 8192, 8192, 128, 128, True,
+                           seed=3, ragged=(1024, 8192)),
+    "cfg4": Decode("cfg4", "bf16", 64, 32, 8, 128, 128, 16, 512, 8192, 512, seed=4),
+    "cfg5": Prefill("cfg5", "f16", 1, 16, 16, 16384, 16384, 128, 128, True, seed=5, hot=10.0),
+}
+
+
+def _normals(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def make_prefill(w: Prefill) -> dict:
+    """Draw Q, K, V (and ragged lengths) for a prefill workload.
+
+    Returns storage arrays ``q``, ``k``, ``v`` (bf16 as uint16 bits),
+    ``seq_lens`` (int32 [B] or None) and ``pads`` (int [B] or None: the number
+    of leading padding rows of each sequence, N - L_b).
+    """
+    rng = np.random.default_rng(w.seed)
+    q32 = _normals(rng, (w.B, w.Hq, w.n, w.d))
+    k32 = _normals(rng, (w.B, w.Hkv, w.m, w.d))
+    v32 = _normals(rng, (w.B, w.Hkv, w.m, w.dv))
+    if w.hot != 1.0:
+        f = np.float32(w.hot)
+        q32 *= f
+        k32 *= f
+    seq_lens = pads = None
+    if w.ragged is not None:
+        lo, hi = w.ragged
+        seq_lens = rng.integers(lo, hi, size=w.B, endpoint=True).astype(np.int32)
+        pads = (w.n - seq_lens).astype(np.int64)
+    q, k, v = store(q32, w.dtype), store(k32, w.dtype), store(v32, w.dtype)
+    del q32, k32, v32
+    if pads is not None:
+        pv = poison_value(w.dtype)
+        for b, p in enumerate(pads):
+            q[b, :, :p] = pv
+            k[b, :, :p] = pv
+            v[b, :, :p] = pv
+    return {"q": q, "k": k, "v": v, "seq_lens": seq_lens, "pads": pads}
+
+
+def make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, dv, seed, hot=1.0, lens=None,
+                        ragged=None) -> dict:
+    """Same recipe at arbitrary (small) sizes, for parity tests."""
+    w = Prefill("custom", dtype, B, Hq, Hkv, n, m, d, dv, False, seed, hot, ragged)
+    out = make_prefill(w)
+    if lens is not None:
+        lens = np.asarray(lens, dtype=np.int32)
+        out["seq_lens"] = lens
+        out["pads"] = (n - lens).astype(np.int64)
+        pv = poison_value(dtype)
+        for b, p in enumerate(out["pads"]):
+            out["q"][b, :, :p] = pv
+            out["k"][b, :, :p] = pv
+            out["v"][b, :, :p] = pv
+    return out
+
+
+def make_decode(w: Decode, seq_lens=None) -> dict:
+    """Draw a paged GQA decode batch.
+
+    Layout: q [S, Hq, d]; k_cache [NB, bs, Hkv, d]; v_cache [NB, bs, Hkv, dv];
+    block_table int32 [S, max_blocks_per_seq] (physical block ids, -1 past the
+    sequence's last block); seq_lens int32 [S].  Physical blocks are a seeded
+    random permutation of 0..NB-1 dealt to the sequences in order.  Cache slots
+    past a sequence's length are NaN.
+    """
+    rng = np.random.default_rng(w.seed)
+    q32 = _normals(rng, (w.num_seqs, w.Hq, w.d))
+    if seq_lens is None:
+        seq_lens = rng.integers(w.len_lo, w.len_hi, size=w.num_seqs, endpoint=True)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    bs = w.block_size
+    nblk = (seq_lens + bs - 1) // bs
+    if nblk.max(initial=0) > w.max_blocks_per_seq:
+        raise ValueError("sequence longer than max_blocks_per_seq * block_size")
+    NB = int(nblk.sum())
+    NBa = max(NB, 1)
+    k32 = _normals(rng, (NBa, bs, w.Hkv, w.d))
+    v32 = _normals(rng, (NBa, bs, w.Hkv, w.dv))
+    perm = rng.permutation(NB).astype(np.int32)
+    table = np.full((w.num_seqs, w.max_blocks_per_seq), -1, dtype=np.int32)
+    pos = 0
+    for s in range(w.num_seqs):
+        c = int(nblk[s])
+        table[s, :c] = perm[pos:pos + c]
+        pos += c
+    q, kc, vc = store(q32, w.dtype), store(k32, w.dtype), store(v32, w.dtype)
+    del q32, k32, v32
+    pv = poison_value(w.dtype)
+    for s in range(w.num_seqs):
+        c = int(nblk[s])
+        tail = int(seq_lens[s]) - (c - 1) * bs if c else bs
+        if c and tail < bs:
+            last = table[s, c - 1]
+            kc[last, tail:] = pv
+            vc[last, tail:] = pv
+    return {"q": q, "k_cache": kc, "v_cache": vc, "block_table": table,
+            "seq_lens": seq_lens.astype(np.int32), "num_blocks": NBa}
+
+
+def prefill_flops(w: Prefill, seq_lens=None) -> float:
+    """Algorithmic FLOPs: 2*d + 2*dv per unmasked (query, key) pair."""
+    per_pair = 2 * w.d + 2 * w.dv
+    if not w.causal:
+        pairs = w.B * w.Hq * w.n * w.m
+    elif seq_lens is None:
+        pairs = w.B * w.Hq * w.n * (w.n + 1) // 2
+    else:
+        L = np.asarray(seq_lens, dtype=np.int64)
+        pairs = int(w.Hq * np.sum(L * (L + 1) // 2))
+    return float(per_pair) * float(pairs)
+
+
+def decode_bytes(w: Decode, seq_lens) -> int:
+    """Algorithmic HBM bytes of one decode call: the K/V rows read once, q, o,
+    the block-table entries used and seq_lens."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    e = ELEM_BYTES[w.dtype]
+    kv = int(L.sum()) * w.Hkv * (w.d + w.dv) * e
+    qo = w.num_seqs * w.Hq * (w.d + w.dv) * e
+    bt = int(((L + w.block_size - 1) // w.block_size).sum()) * 4
+    return kv + qo + bt + 4 * w.num_seqs
