@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the attention hot path on one MI355X.
+
+One step = one prefill call (bf16, B=4, H=32, n=m=2048, d=128, non-causal, the
+workload the headline metric is quoted on) followed by one paged GQA decode call
+(64 sequences, 32 query / 8 KV heads, d=128, blocks of 16, lengths in
+[512, 8192]).  Inputs are seeded synthetic tensors resident in device memory
+before timing starts.  Prints one JSON line:
+
+  value     prefill TFLOP/s (algorithmic: 4*d FLOP per (query, key) pair)
+  roofline  the prefill kernel against the bf16 dense MFMA peak
+  decode    paged decode GB/s (algorithmic bytes) against HBM peak
+  cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_prefill.hip",
+                   "tiled_online_softmax_04_amd/csrc/fa_common.h"]
+DECODE_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_decode.hip",
+                  "tiled_online_softmax_04_amd/csrc/fa_common.h"]
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, paths):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is absent or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest(paths):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """Time the float64 oracle on whole (batch, head) slices of the workload until
+    about `budget_s` seconds of CPU work, and scale to TFLOP/s."""
+    import oracle
+    from tiled_online_softmax_04_amd import inputs as gen
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    done, t_used, flops = 0, 0.0, 0.0
+    per_head = 4.0 * w.n * w.m * w.d
+    for b, h in heads:
+        q = gen.to_f64(x["q"][b:b + 1, h:h + 1], w.dtype)
+        k = gen.to_f64(x["k"][b:b + 1, h:h + 1], w.dtype)
+        v = gen.to_f64(x["v"][b:b + 1, h:h + 1], w.dtype)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.scale, w.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        flops += per_head
+        if t_used >= budget_s:
+            break
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s",
+            "cores": int(min(threads, len(os.sched_getaffinity(0)))), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (batch, head) slices of the same workload, "
+                      f"float64, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 skips it)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single GPU; runs on more than one GPU are not part of "
+              "this build (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_online_softmax_04_amd import fa
+    from tiled_online_softmax_04_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    wp = gen.WORKLOADS["cfg2"]
+    xp = gen.make_prefill(wp)
+    q, k, v = (to_dev(xp[n], wp.dtype) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+
+    wd = gen.WORKLOADS["cfg4"]
+    xd = gen.make_decode(wd)
+    dq = to_dev(xd["q"], wd.dtype)
+    kc, vc = to_dev(xd["k_cache"], wd.dtype), to_dev(xd["v_cache"], wd.dtype)
+    bt = torch.from_numpy(xd["block_table"]).to(dev)
+    sl = torch.from_numpy(xd["seq_lens"]).to(dev)
+    do = torch.empty((wd.num_seqs, wd.Hq, wd.dv), dtype=dq.dtype, device=dev)
+    ws_bytes = fa.paged_decode_workspace_size(wd.num_seqs, wd.Hq, wd.Hkv, wd.dv,
+                                              wd.max_blocks_per_seq, wd.block_size)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    if args.copy_probe_mib > 0:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fwd(q, k, v, scale=wp.scale, causal=wp.causal, out=o)
+        if ev is not None:
+            ev[1].record()
+        fa.paged_decode(dq, kc, vc, bt, sl, wd.block_size, scale=wd.scale, out=do, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    flops = gen.prefill_flops(wp)
+    dbytes = gen.decode_bytes(wd, xd["seq_lens"])
+    pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
+    dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
+
+    traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
+    dec_traffic = read_traffic("fa_decode_cfg4_traffic.txt", DECODE_SOURCES)
+
+    baseline = None
+    if args.cpu_budget > 0:
+        baseline = cpu_baseline(wp, xp, args.cpu_budget)
+
+    out = {
+        "metric": "attn fwd TFLOP/s + % bf16 MFMA peak; paged decode GB/s + % HBM peak",
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill bf16 B=4 H=32 n=m=2048 d=dv=128 non-causal, "
+                               "then paged GQA decode bf16 64 seqs Hq=32 Hkv=8 d=128 block 16 "
+                               "lengths U[512,8192]",
+                   "prefill_flop": flops, "decode_bytes": dbytes, "seed_prefill": wp.seed,
+                   "seed_decode": wd.seed},
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "fa_fwd_mfma<BF16,128,false,false>",
+                     "avg_launch_ms": round(float(pre_ms.mean()), 5)},
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                "traffic": dec_traffic,
+                                "kernels": "fa_decode_split + fa_decode_merge",
+                                "avg_call_ms": round(float(dec_ms.mean()), 5)}},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * fa.h -- C ABI of the gfx950 tiled online-softmax attention library (libfa.so).
+ *
+ * The library computes exact scaled-dot-product attention, O = softmax(S) V with
+ * S = scale * Q K^T, as one pass over key tiles with an online softmax: a running
+ * row max m, a running sum l and an accumulator acc, both rescaled by
+ * exp(m_old - m_new) whenever the max moves, so the n x m score matrix never
+ * reaches device memory.  The operation is the one stated in section 1 of
+ * "手搓 Attention：从三行循环到看懂 FlashAttention" (10100.com): Q has n rows,
+ * K has m rows, both of width d; V has m rows of width dv; O has n rows of
+ * width dv.  The recurrence is that article's section 7 and the "核心思路"
+ * section of the FlashAttention chapter (llminference.xinbetween.com S12).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named q, k, v, o, k_cache, v_cache, block_table, seq_lens and
+ *    workspace are DEVICE pointers, allocated and owned by the caller.  The
+ *    library allocates nothing, frees nothing and keeps no state between calls
+ *    except a per-thread text of the last error (fa_last_error).
+ *  - Tensors are dense, row-major, with the shapes given below; element pointers
+ *    must be 16-byte aligned.  All of q, k, v and o share one dtype.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    null stream) and the call returns without synchronising.  Results are
+ *    valid once the caller has synchronised that stream.
+ *  - Arguments are checked on the host before any HIP call; on any status other
+ *    than FA_OK nothing has been launched (FA_ERR_HIP excepted: it reports a
+ *    launch failure).  The host never reads device memory: values inside
+ *    seq_lens or block_table that break the stated ranges are undefined
+ *    behaviour.
+ *  - Every call is deterministic: the same inputs give bitwise the same output.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_DTYPE_F32 = 0,  /* float32 in and out; scores and the softmax shift in float64 */
+  FA_DTYPE_F16 = 1,  /* float16 in and out; MFMA with float32 accumulation        */
+  FA_DTYPE_BF16 = 2  /* bfloat16 in and out; MFMA with float32 accumulation       */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,      /* an argument breaks the contract (null, range, shape)   */
+  FA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement            */
+  FA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required             */
+  FA_ERR_HIP = 4           /* the HIP runtime reported an error (see fa_last_error)  */
+} fa_status;
+
+/*
+ * fa_fwd -- batched prefill attention.
+ *
+ *   q [batch, heads_q,  n, d ]    k [batch, heads_kv, m, d ]
+ *   v [batch, heads_kv, m, dv]    o [batch, heads_q,  n, dv]   (o is written)
+ *
+ * Query head h reads key/value head h / (heads_q / heads_kv) (grouped heads as in
+ * the S12 chapter's "它如何与你已经搭好的部分组合" section).
+ *
+ * scale   : multiplies Q K^T; finite and > 0.  1/sqrt(d) is the usual value (10100.com
+ *           section 1, S12 "核心思路"); the 5688vip example uses 1.
+ * causal  : nonzero -> query i may attend key j only when j <= i (keys 0..i, the
+ *           causal variant of 10100.com section 6).  Requires n == m.
+ * seq_lens: NULL, or a device int32[batch] of left-padded lengths 0 <= L_b <= n.
+ *           Requires n == m.  Sequence b occupies positions [n - L_b, n) of both
+ *           queries and keys; positions before that are padding, are never read
+ *           into the arithmetic (they may hold anything, NaN included) and their
+ *           output rows are written as 0.  Combined with causal this gives the
+ *           ragged causal batch of the S12 NaN note ("exp(-inf - -inf) 是 NaN").
+ * A query row with no allowed key gets O = 0 (never NaN).
+ *
+ * Limits of this build: d == dv, d in {64, 128} (else FA_ERR_UNSUPPORTED).
+ * FA_ERR_INVALID: a null tensor pointer (when the tensor is non-empty), negative
+ *   sizes, heads_kv == 0 or heads_q % heads_kv != 0, causal or seq_lens with
+ *   n != m, a non-finite or non-positive scale, misaligned pointers, an unknown
+ *   dtype, or sizes beyond 2^31 elements per head dimension product.
+ * Empty work (batch, heads_q or n zero) returns FA_OK without launching.
+ */
+fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
+                 int batch, int heads_q, int heads_kv, int n, int m, int d, int dv,
+                 float scale, int causal, const int32_t* seq_lens, void* stream);
+
+/*
+ * fa_paged_decode_workspace_size -- bytes of device workspace fa_paged_decode needs
+ * for these sizes (the split-K partial states).  Depends only on its arguments.
+ * Returns 0 for arguments fa_paged_decode would reject.
+ */
+size_t fa_paged_decode_workspace_size(int num_seqs, int heads_q, int heads_kv, int dv,
+                                      int max_blocks_per_seq, int block_size);
+
+/*
+ * fa_paged_decode -- one query token per sequence over a paged KV cache, with
+ * grouped-query heads, split over key ranges and merged (flash-decoding).
+ *
+ * Follows the paged loop of the S12 chapter ("实现": walk the block table, the
+ * last block holding min(block_size, seq_len - t * block_size) tokens, stop at the
+ * first empty block) inside the online-softmax recurrence, with the key ranges
+ * spread over workgroups and their (m, l, o) states merged by the same rescale
+ * (S12 "除了快，它还解锁了什么" and exercise 1).
+ *
+ *   q           [num_seqs, heads_q, d]
+ *   k_cache     [num_blocks, block_size, heads_kv, d ]
+ *   v_cache     [num_blocks, block_size, heads_kv, dv]
+ *   block_table [num_seqs, max_blocks_per_seq] int32: physical block of each
+ *               logical block; entries at or past ceil(L_b / block_size) are
+ *               never read (they may hold -1).  Used entries must be in
+ *               [0, num_blocks).
+ *   seq_lens    [num_seqs] int32, 0 <= L_b <= max_blocks_per_seq * block_size.
+ *               Cache slots past L_b are never read into the arithmetic.  L_b = 0
+ *               gives O = 0.
+ *   o           [num_seqs, heads_q, dv] (written)
+ *   workspace   device buffer of at least fa_paged_decode_workspace_size(...)
+ *               bytes, owned by the caller; its contents on entry do not matter.
+ *
+ * Query head h reads KV head h / (heads_q / heads_kv).
+ * Limits of this build: dtype f16 or bf16 (f32 -> FA_ERR_UNSUPPORTED); d == dv,
+ * d in {64, 128}.
+ * FA_ERR_INVALID: null pointers for non-empty work, non-positive block_size,
+ *   num_blocks or max_blocks_per_seq, negative sizes, heads_q % heads_kv != 0,
+ *   non-finite or non-positive scale, misaligned pointers.
+ * FA_ERR_WORKSPACE: workspace_bytes below the required size (or a null workspace).
+ * Two kernels are enqueued: the split pass and the merge pass.
+ */
+fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                          int num_seqs, int heads_q, int heads_kv, int d, int dv,
+                          int num_blocks, int max_blocks_per_seq, float scale, void* o,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

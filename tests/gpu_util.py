@@ -1,0 +1,47 @@
+"""Helpers shared by the GPU tests: moving storage arrays to the device and back,
+and the error metrics of the parity bar."""
+import sys
+
+import numpy as np
+
+from tiled_online_softmax_04_amd import inputs as gen
+
+# Parity bar: fp32 inputs max abs <= 1e-5; bf16/fp16 max abs <= 1e-2 and mean
+# abs <= 1e-3 against the oracle on the identically rounded inputs.
+TOL = {"f32": (1e-5, 1e-5), "f16": (1e-2, 1e-3), "bf16": (1e-2, 1e-3)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(stored: np.ndarray, dtype: str):
+    import torch
+    a = np.ascontiguousarray(stored)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def to_f64(t, dtype: str) -> np.ndarray:
+    import torch
+    if dtype == "bf16":
+        return gen.bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.float().cpu().numpy().astype(np.float64) if dtype == "f16" else \
+        t.cpu().numpy().astype(np.float64)
+
+
+def metrics(got: np.ndarray, ref: np.ndarray):
+    bad = int((~np.isfinite(got)).sum())
+    diff = np.abs(np.where(np.isfinite(got), got, 0.0) - ref)
+    return float(diff.max(initial=0.0)), float(diff.mean()) if diff.size else 0.0, bad
+
+
+def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, label: str = ""):
+    mx, mean, bad = metrics(got, ref)
+    tmax, tmean = TOL[dtype]
+    say(f"  {label}: max_abs={mx:.3e} mean_abs={mean:.3e} nonfinite={bad}")
+    assert bad == 0, f"{label}: {bad} non-finite outputs"
+    assert mx <= tmax, f"{label}: max abs {mx:.3e} > {tmax}"
+    assert mean <= tmean, f"{label}: mean abs {mean:.3e} > {tmean}"

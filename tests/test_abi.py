@@ -1,0 +1,137 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fa.h, and rejects bad arguments before any HIP call.
+
+Every call below is meant to fail validation; none may reach a launch (the
+pointers are placeholders, never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiled_online_softmax_04_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+P = ctypes.c_void_p(0x100000)   # aligned placeholder, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x100008)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (python -m tiled_online_softmax_04_amd.build)")
+    return fa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["fa_fwd", "fa_last_error", "fa_paged_decode",
+                                    "fa_paged_decode_workspace_size", "fa_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code, word in [(0, "ok"), (1, "invalid"), (2, "unsupported"), (3, "workspace"), (4, "HIP")]:
+        assert word in lib.fa_status_string(code).decode()
+
+
+def fwd(lib, dt=2, q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, n=128, m=128, d=128, dv=128,
+        scale=0.088, causal=0, seq_lens=None):
+    return lib.fa_fwd(dt, q, k, v, o, B, Hq, Hkv, n, m, d, dv, scale, causal, seq_lens, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), fa.FA_ERR_INVALID),
+    (dict(B=-1), fa.FA_ERR_INVALID),
+    (dict(d=0), fa.FA_ERR_INVALID),
+    (dict(Hkv=0), fa.FA_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(causal=1, m=64), fa.FA_ERR_INVALID),
+    (dict(seq_lens=P, m=64), fa.FA_ERR_INVALID),
+    (dict(scale=0.0), fa.FA_ERR_INVALID),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(n=1 << 24, m=1 << 24), fa.FA_ERR_INVALID),
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, dv=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256, dv=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=None), fa.FA_ERR_INVALID),
+    (dict(o=None), fa.FA_ERR_INVALID),
+    (dict(k=None), fa.FA_ERR_INVALID),
+    (dict(v=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(q=MISALIGNED), fa.FA_ERR_INVALID),
+])
+def test_fwd_rejects_before_launch(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fwd_empty_work_is_ok_without_pointers(lib):
+    assert fwd(lib, q=None, k=None, v=None, o=None, B=0) == fa.FA_OK
+    assert fwd(lib, q=None, k=None, v=None, o=None, n=0, m=0) == fa.FA_OK
+    assert lib.fa_last_error().decode() == ""
+
+
+def dec(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, dv=128, NB=64,
+        maxb=16, scale=0.088, o=P, ws=P, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_paged_decode_workspace_size(S, Hq, Hkv, dv, maxb, bs) if S >= 0 else 0
+    return lib.fa_paged_decode(dt, q, kc, vc, bt, sl, bs, S, Hq, Hkv, d, dv, NB, maxb, scale, o,
+                               ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), fa.FA_ERR_INVALID),
+    (dict(bs=0), fa.FA_ERR_INVALID),
+    (dict(maxb=0), fa.FA_ERR_INVALID),
+    (dict(NB=0), fa.FA_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(Hkv=0), fa.FA_ERR_INVALID),
+    (dict(S=-2), fa.FA_ERR_INVALID),
+    (dict(S=70000), fa.FA_ERR_INVALID),
+    (dict(scale=0.0), fa.FA_ERR_INVALID),
+    (dict(d=80, dv=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(bt=None), fa.FA_ERR_INVALID),
+    (dict(sl=None), fa.FA_ERR_INVALID),
+    (dict(kc=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_launch(lib, kw, code):
+    assert dec(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_decode_workspace_size(lib):
+    # 64 sequences x 32 query heads, up to 512 blocks of 16 keys: 512-key splits
+    # -> 16 splits, each holding (m, l, acc[128]) in float32
+    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * 130 * 4
+    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 0, 16) == 0
+    assert lib.fa_paged_decode_workspace_size(64, 32, 0, 128, 512, 16) == 0
+    # a lone sequence gets smaller splits so the GPU still fills
+    one = lib.fa_paged_decode_workspace_size(1, 32, 8, 128, 512, 16)
+    assert one > 32 * 16 * 130 * 4
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
+same seeded inputs.  Small shapes are compared element by element; the full
+workload sizes are checked on sampled outputs and on properties that hold at
+any size (no inf/NaN, padding rows exactly 0, causal first row equal to V's)."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tiled_online_softmax_04_amd import fa
+from tiled_online_softmax_04_amd import inputs as gen
+
+from gpu_util import assert_parity, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(x, dtype, causal, scale, pads):
+    import torch
+    q, k, v = to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype)
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).cuda()
+    o = fa.fwd(q, k, v, scale=scale, causal=causal, seq_lens=sl)
+    torch.cuda.synchronize()
+    return o
+
+
+def f64_inputs(x, dtype):
+    return (gen.to_f64(x["q"], dtype), gen.to_f64(x["k"], dtype), gen.to_f64(x["v"], dtype))
+
+
+SMALL = [
+    # name, dtype, B, Hq, Hkv, n, m, d, causal, hot, lens
+    ("bf16_noncausal_tail", "bf16", 2, 4, 4, 300, 300, 128, False, 1.0, None),
+    ("bf16_causal_333", "bf16", 1, 3, 3, 333, 333, 128, True, 1.0, None),
+    ("f16_causal_hot", "f16", 1, 2, 2, 520, 520, 128, True, 10.0, None),
+    ("bf16_causal_leftpad", "bf16", 4, 2, 2, 400, 400, 128, True, 1.0, [400, 1, 0, 137]),
+    ("bf16_noncausal_leftpad", "bf16", 3, 2, 2, 260, 260, 128, False, 1.0, [260, 64, 5]),
+    ("bf16_gqa_d64_causal", "bf16", 1, 8, 2, 200, 200, 64, True, 1.0, None),
+    ("f16_n_ne_m", "f16", 2, 2, 1, 100, 333, 128, False, 1.0, None),
+    ("f16_d64_noncausal", "f16", 1, 4, 4, 129, 129, 64, False, 1.0, None),
+    ("bf16_single_row", "bf16", 1, 1, 1, 1, 1, 128, True, 1.0, None),
+    ("bf16_single_key", "bf16", 1, 2, 2, 70, 1, 64, False, 1.0, None),
+    ("bf16_hot_noncausal_d64", "bf16", 2, 2, 2, 256, 256, 64, False, 10.0, None),
+    ("f32_causal_leftpad_hot", "f32", 2, 2, 2, 100, 100, 64, True, 10.0, [100, 33]),
+    ("f32_d128_gqa_causal", "f32", 1, 4, 2, 77, 77, 128, True, 1.0, None),
+    ("f32_noncausal_n_ne_m", "f32", 1, 2, 2, 50, 90, 128, False, 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_prefill_small(case):
+    name, dtype, B, Hq, Hkv, n, m, d, causal, hot, lens = case
+    say(f"[prefill] {name}")
+    x = gen.make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, d,
+                                seed=zlib.crc32(name.encode()) % 1000, hot=hot, lens=lens)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    o = run_prefill(x, dtype, causal, scale, x["pads"])
+    got = to_f64(o, dtype)
+    q, k, v = f64_inputs(x, dtype)
+    ref = oracle.attention(q, k, v, scale, causal, pads=x["pads"])
+    assert_parity(got, ref, dtype, name)
+    if x["pads"] is not None:
+        for b, p in enumerate(x["pads"]):
+            assert np.all(got[b, :, :p] == 0), "padding rows must be exactly 0"
+    if causal and n == m:
+        for b in range(B):
+            p = 0 if x["pads"] is None else int(x["pads"][b])
+            if p < n:   # first real row attends only its own key: O = V exactly
+                for h in range(Hq):
+                    assert np.array_equal(got[b, h, p], v[b, h // (Hq // Hkv), p])
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg1_hot"])
+def test_cfg1_fp32(name):
+    w = gen.WORKLOADS[name]
+    say(f"[prefill] {name}")
+    x = gen.make_prefill(w)
+    o = run_prefill(x, "f32", w.causal, w.scale, None)
+    q, k, v = f64_inputs(x, "f32")
+    ref = oracle.attention(q, k, v, w.scale, w.causal)
+    assert_parity(to_f64(o, "f32"), ref, "f32", name)
+
+
+def test_empty_key_set_gives_zero():
+    import torch
+    say("[prefill] no keys")
+    q = torch.randn(1, 2, 40, 128, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
+    o = fa.fwd(q, k, k)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+
+
+def test_prefill_deterministic():
+    import torch
+    say("[prefill] determinism")
+    x = gen.make_prefill_custom("bf16", 1, 4, 4, 700, 700, 128, 128, seed=5, lens=[650])
+    a = run_prefill(x, "bf16", True, 0.088, x["pads"])
+    b = run_prefill(x, "bf16", True, 0.088, x["pads"])
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# full workload sizes: sampled outputs + whole-tensor properties
+# --------------------------------------------------------------------------
+def samples_for(w, pads, rng, count=40):
+    out = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.n - 1), (0, w.Hq // 2, 127), (0, 1, 128),
+           (w.B - 1, 0, w.n // 2)]
+    if pads is not None:
+        for b, p in enumerate(pads):
+            out += [(b, b % w.Hq, int(min(p, w.n - 1))), (b, (b + 1) % w.Hq, int(max(p - 1, 0)))]
+    while len(out) < count:
+        out.append((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.n))))
+    return out
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_ragged", "cfg5"])
+def test_full_size_sampled(name):
+    import torch
+    w = gen.WORKLOADS[name]
+    say(f"[prefill] {name} generating")
+    x = gen.make_prefill(w)
+    say(f"[prefill] {name} running")
+    o = run_prefill(x, w.dtype, w.causal, w.scale, x["pads"])
+    assert bool(torch.isfinite(o.float()).all()), "non-finite outputs"
+    if x["pads"] is not None:
+        for b, p in enumerate(x["pads"]):
+            assert bool((o[b, :, :int(p)] == 0).all())
+    say(f"[prefill] {name} oracle on samples")
+    rng = np.random.default_rng(100 + w.seed)
+    samples = samples_for(w, x["pads"], rng)
+    qs = gen.to_f64(x["q"], w.dtype) if w.B * w.n <= 8192 else None
+    # upcast only the heads the samples touch (the ragged batch is large)
+    got = np.stack([to_f64(o[b, h, i], w.dtype) for b, h, i in samples])
+    ref = np.zeros_like(got)
+    for t, (b, h, i) in enumerate(samples):
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        if i < pad:
+            continue
+        qrow = gen.to_f64(x["q"][b, h, i], w.dtype)[None] if qs is None else qs[b, h, i][None]
+        kk = gen.to_f64(x["k"][b, h // (w.Hq // w.Hkv)], w.dtype)
+        vv = gen.to_f64(x["v"][b, h // (w.Hq // w.Hkv)], w.dtype)
+        ref[t] = oracle.attend(qrow, [i], kk, vv, w.scale, w.causal, pad)[0]
+    assert_parity(got, ref, w.dtype, f"{name} ({len(samples)} sampled rows)")
+    if w.causal:
+        p0 = 0 if x["pads"] is None else int(x["pads"][0])
+        if p0 < w.n:
+            row = to_f64(o[0, 0, p0], w.dtype)
+            assert np.array_equal(row, gen.to_f64(x["v"][0, 0, p0], w.dtype))
+
+
+# --------------------------------------------------------------------------
+# paged decode
+# --------------------------------------------------------------------------
+def run_decode(x, dtype, bs, scale):
+    import torch
+    q = to_dev(x["q"], dtype)
+    kc, vc = to_dev(x["k_cache"], dtype), to_dev(x["v_cache"], dtype)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seq_lens"]).cuda()
+    o = fa.paged_decode(q, kc, vc, bt, sl, bs, scale=scale)
+    torch.cuda.synchronize()
+    return o
+
+
+def decode_oracle(x, dtype, bs, scale):
+    return oracle.paged_decode(gen.to_f64(x["q"], dtype), gen.to_f64(x["k_cache"], dtype),
+                               gen.to_f64(x["v_cache"], dtype), x["block_table"], x["seq_lens"],
+                               bs, scale)
+
+
+DEC_SMALL = [
+    # name, dtype, S, Hq, Hkv, d, bs, lens, maxb
+    ("bf16_g4_d128", "bf16", 6, 8, 2, 128, 16, [1, 15, 16, 17, 700, 0], 50),
+    ("f16_g4_d128", "f16", 4, 32, 8, 128, 16, [513, 2000, 64, 1030], 130),
+    ("bf16_g1_d64", "bf16", 3, 4, 4, 64, 16, [100, 1, 257], 20),
+    ("bf16_g2_bs7", "bf16", 3, 4, 2, 128, 7, [50, 6, 700], 100),
+    ("f16_g8_d64", "f16", 2, 16, 2, 64, 32, [1500, 33], 50),
+    ("bf16_one_seq_long", "bf16", 1, 32, 8, 128, 16, [8192], 512),
+]
+
+
+@pytest.mark.parametrize("case", DEC_SMALL, ids=[c[0] for c in DEC_SMALL])
+def test_decode_small(case):
+    name, dtype, S, Hq, Hkv, d, bs, lens, maxb = case
+    say(f"[decode] {name}")
+    w = gen.Decode(name, dtype, S, Hq, Hkv, d, d, bs, 1, 1, maxb, seed=len(name))
+    x = gen.make_decode(w, seq_lens=lens)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = to_f64(run_decode(x, dtype, bs, scale), dtype)
+    ref = decode_oracle(x, dtype, bs, scale)
+    assert_parity(got, ref, dtype, name)
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[s] == 0)
+
+
+def test_decode_cfg4_full():
+    w = gen.WORKLOADS["cfg4"]
+    say("[decode] cfg4 generating")
+    x = gen.make_decode(w)
+    say("[decode] cfg4 running")
+    got = to_f64(run_decode(x, w.dtype, w.block_size, w.scale), w.dtype)
+    say("[decode] cfg4 oracle")
+    ref = decode_oracle(x, w.dtype, w.block_size, w.scale)
+    assert_parity(got, ref, w.dtype, "cfg4 (all outputs)")
+
+
+def test_decode_block_placement_invariance_and_determinism():
+    import torch
+    say("[decode] block placement")
+    w = gen.Decode("perm", "bf16", 8, 32, 8, 128, 128, 16, 100, 3000, 200, seed=77)
+    x = gen.make_decode(w)
+    a = run_decode(x, "bf16", 16, w.scale)
+    b = run_decode(x, "bf16", 16, w.scale)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # move every physical block elsewhere and rewrite the table to match
+    NB = x["k_cache"].shape[0]
+    perm = np.random.default_rng(5).permutation(NB)
+    y = dict(x)
+    y["k_cache"] = np.empty_like(x["k_cache"])
+    y["v_cache"] = np.empty_like(x["v_cache"])
+    y["k_cache"][perm] = x["k_cache"]
+    y["v_cache"][perm] = x["v_cache"]
+    t = x["block_table"].copy()
+    t[t >= 0] = perm[t[t >= 0]]
+    y["block_table"] = t
+    c = run_decode(y, "bf16", 16, w.scale)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))

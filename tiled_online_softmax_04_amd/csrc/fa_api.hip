@@ -1,0 +1,154 @@
+// C ABI of libfa.so: argument checks, dispatch, error reporting.  See include/fa.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+fa_status hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+constexpr long long kMaxElems = 1LL << 31;
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace too small";
+    case FA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o, int batch,
+                 int heads_q, int heads_kv, int n, int m, int d, int dv, float scale, int causal,
+                 const int32_t* seq_lens, void* stream) {
+  g_last_error[0] = '\0';
+  if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  if (batch < 0 || heads_q < 0 || heads_kv < 0 || n < 0 || m < 0 || d <= 0 || dv <= 0)
+    return fail(FA_ERR_INVALID, "negative or zero size (batch=%d heads_q=%d heads_kv=%d n=%d "
+                "m=%d d=%d dv=%d)", batch, heads_q, heads_kv, n, m, d, dv);
+  if (heads_kv == 0 && heads_q != 0) return fail(FA_ERR_INVALID, "heads_kv is 0");
+  if (heads_kv != 0 && heads_q % heads_kv != 0)
+    return fail(FA_ERR_INVALID, "heads_q (%d) is not a multiple of heads_kv (%d)", heads_q,
+                heads_kv);
+  if (causal && n != m) return fail(FA_ERR_INVALID, "causal needs n == m (n=%d m=%d)", n, m);
+  if (seq_lens && n != m)
+    return fail(FA_ERR_INVALID, "seq_lens (left padding) needs n == m (n=%d m=%d)", n, m);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
+  if ((long long)n * d >= kMaxElems || (long long)m * d >= kMaxElems ||
+      (long long)n * dv >= kMaxElems || (long long)m * dv >= kMaxElems)
+    return fail(FA_ERR_INVALID, "one head holds 2^31 elements or more");
+  if (!supported_head_dim(d) || dv != d)
+    return fail(FA_ERR_UNSUPPORTED, "head dims d=%d dv=%d (need d == dv in {64, 128})", d, dv);
+  if (batch == 0 || heads_q == 0 || n == 0) return FA_OK;
+  if (!q || !o) return fail(FA_ERR_INVALID, "null q or o");
+  if (m > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "null k or v");
+  if (!aligned16(q) || !aligned16(o) || (m > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const long long grid = fa::fwd_grid_size((int)dt, batch, heads_q, n);
+  if (grid >= (1LL << 31)) return fail(FA_ERR_INVALID, "grid too large (%lld)", grid);
+
+  fa::FwdArgs a{(int)dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, scale, causal ? 1 : 0,
+                seq_lens, stream};
+  const hipError_t e = fa::launch_fwd(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
+  return FA_OK;
+}
+
+static fa_status check_decode_sizes(int num_seqs, int heads_q, int heads_kv, int d, int dv,
+                                    int max_blocks_per_seq, int block_size) {
+  if (num_seqs < 0 || heads_q < 0 || heads_kv <= 0 || d <= 0 || dv <= 0)
+    return fail(FA_ERR_INVALID, "bad sizes (num_seqs=%d heads_q=%d heads_kv=%d d=%d dv=%d)",
+                num_seqs, heads_q, heads_kv, d, dv);
+  if (block_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(FA_ERR_INVALID, "block_size (%d) and max_blocks_per_seq (%d) must be > 0",
+                block_size, max_blocks_per_seq);
+  if (heads_q % heads_kv != 0)
+    return fail(FA_ERR_INVALID, "heads_q (%d) is not a multiple of heads_kv (%d)", heads_q,
+                heads_kv);
+  if (num_seqs > 65535) return fail(FA_ERR_INVALID, "num_seqs above 65535");
+  if ((long long)max_blocks_per_seq * block_size >= (1LL << 31))
+    return fail(FA_ERR_INVALID, "max_blocks_per_seq * block_size overflows int32");
+  if (!supported_head_dim(d) || dv != d)
+    return fail(FA_ERR_UNSUPPORTED, "head dims d=%d dv=%d (need d == dv in {64, 128})", d, dv);
+  return FA_OK;
+}
+
+size_t fa_paged_decode_workspace_size(int num_seqs, int heads_q, int heads_kv, int dv,
+                                      int max_blocks_per_seq, int block_size) {
+  if (check_decode_sizes(num_seqs, heads_q, heads_kv, dv, dv, max_blocks_per_seq, block_size) !=
+      FA_OK)
+    return 0;
+  const fa::DecodePlan p =
+      fa::decode_plan(num_seqs, heads_q, heads_kv, max_blocks_per_seq, block_size);
+  return fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
+}
+
+fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                          int num_seqs, int heads_q, int heads_kv, int d, int dv, int num_blocks,
+                          int max_blocks_per_seq, float scale, void* o, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  fa_status s = check_decode_sizes(num_seqs, heads_q, heads_kv, d, dv, max_blocks_per_seq,
+                                   block_size);
+  if (s != FA_OK) return s;
+  if (num_blocks <= 0) return fail(FA_ERR_INVALID, "num_blocks must be > 0");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
+  if ((long long)num_blocks * block_size * heads_kv * d >= (1LL << 40))
+    return fail(FA_ERR_INVALID, "cache larger than 2^40 elements");
+  if (dt == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "paged decode supports f16 and bf16");
+  if (num_seqs == 0 || heads_q == 0) return FA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+    return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const fa::DecodePlan p =
+      fa::decode_plan(num_seqs, heads_q, heads_kv, max_blocks_per_seq, block_size);
+  const size_t need = fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                need);
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID, "workspace must be 16-byte aligned");
+
+  fa::DecodeArgs a{(int)dt, q,        k_cache,  v_cache,    block_table,        seq_lens,
+                   block_size, num_seqs, heads_q, heads_kv, d, num_blocks, max_blocks_per_seq,
+                   scale, o, workspace, stream};
+  const hipError_t e = fa::launch_decode(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_paged_decode launch");
+  return FA_OK;
+}
+
+}  // extern "C"

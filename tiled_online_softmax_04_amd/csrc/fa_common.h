@@ -1,0 +1,97 @@
+// Device helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+// log2(e): the kernels work with exp2 and fold log2(e) into the fp32 score scale.
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite start for the running max (in scaled log2 units).  Masked scores are
+// -inf, so exp2(-inf - kSentinel) = 0 and a fully masked tile leaves the state
+// untouched instead of producing exp2(-inf - -inf) = NaN.
+constexpr float kSentinel = -1.0e30f;
+
+// ---------------------------------------------------------------------------
+// 16-bit storage types.  Values travel as raw 16-bit patterns (uint16_t in
+// memory, packed pairs in uint32_t registers).
+// ---------------------------------------------------------------------------
+struct BF16 {
+  static __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // Round two floats to nearest-even and pack (lo in bits 0..15).
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+};
+
+struct F16 {
+  static __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xffffu));
+  }
+  static __device__ __forceinline__ float hi(uint32_t x) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane moves within rows of 16 lanes (bound_ctrl: out-of-row reads give 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int kRowRor8 = 0x128;      // lane i <- lane (i+8) mod 16 within a row
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Return a
+// logical id such that each XCD receives one contiguous range of logical ids,
+// so neighbouring tiles (which share K/V) meet in one XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int x = bid % kXcd, k = bid / kXcd;
+  const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + k;
+}
+
+}  // namespace fa

@@ -1,0 +1,53 @@
+// Internal interface between the C ABI (fa_api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  int dtype;  // 0 f32, 1 f16, 2 bf16 (fa_dtype values)
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int batch, heads_q, heads_kv, n, m, d;
+  float scale;
+  int causal;
+  const int32_t* seq_lens;
+  void* stream;
+};
+
+struct DecodeArgs {
+  int dtype;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int block_size, num_seqs, heads_q, heads_kv, d, num_blocks, max_blocks_per_seq;
+  float scale;
+  void* o;
+  void* workspace;
+  void* stream;
+};
+
+// Number of workgroups fa_fwd launches (the host checks it fits a grid).
+long long fwd_grid_size(int dtype, int batch, int heads_q, int n);
+hipError_t launch_fwd(const FwdArgs& a);
+
+// Split size (tokens) and split count of the paged decode, from sizes only.
+struct DecodePlan {
+  int split_tokens;  // keys per split workgroup
+  int max_splits;    // splits per sequence at max_blocks_per_seq * block_size keys
+  int heads_per_wg;  // query heads of one KV group handled by one workgroup
+  int subgroups;     // workgroups per (sequence, KV head, split)
+};
+DecodePlan decode_plan(int num_seqs, int heads_q, int heads_kv, int max_blocks_per_seq,
+                       int block_size);
+size_t decode_workspace_bytes(const DecodePlan& p, int num_seqs, int heads_q, int dv);
+hipError_t launch_decode(const DecodeArgs& a);
+
+}  // namespace fa

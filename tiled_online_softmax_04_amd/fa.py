@@ -1,0 +1,181 @@
+"""Thin ctypes binding of libfa.so (declared in include/fa.h).
+
+Only argument marshalling happens here: shapes and dtypes are read off the torch
+tensors, device pointers and the current HIP stream are passed to the C ABI,
+and status codes become exceptions.  Every step of the attention itself runs
+in the library's kernels.  Missing library -> RuntimeError; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+_lib = None
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once.  torch is imported first so that the library binds to
+    the HIP runtime torch already loaded (one runtime per process)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (loads libamdhip64 before libfa.so resolves it)
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m tiled_online_softmax_04_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.restype = _c_int
+    lib.fa_fwd.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                           ctypes.c_float, _c_int, _c_void_p, _c_void_p]
+    lib.fa_paged_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fa_paged_decode_workspace_size.argtypes = [_c_int] * 6
+    lib.fa_paged_decode.restype = _c_int
+    lib.fa_paged_decode.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    ctypes.c_float, _c_void_p, _c_void_p, ctypes.c_size_t,
+                                    _c_void_p]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [_c_int]
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+class FAError(RuntimeError):
+    pass
+
+
+def check(status: int) -> None:
+    if status == FA_OK:
+        return
+    lib = load_library()
+    msg = f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}"
+    if status in (FA_ERR_INVALID, FA_ERR_WORKSPACE):
+        raise ValueError(msg)
+    if status == FA_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise FAError(msg)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, ndim, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens=None, out=None,
+        stream=None):
+    """O = softmax(scale * Q K^T [masked]) V.  q [B, Hq, n, d], k [B, Hkv, m, d],
+    v [B, Hkv, m, dv] on one device, one dtype; seq_lens: None or int32 [B]
+    left-padded lengths.  scale defaults to 1/sqrt(d)."""
+    import torch
+    lib = load_library()
+    _require(q, "q", 4, q.device)
+    _require(k, "k", 4, q.device)
+    _require(v, "v", 4, q.device)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, n, d = q.shape
+    Bk, Hkv, m, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape[:3]) != (B, Hkv, m):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    dv = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if seq_lens is not None:
+        _require(seq_lens, "seq_lens", 1, q.device)
+        if seq_lens.dtype != torch.int32 or seq_lens.shape[0] != B:
+            raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, n, dv), dtype=q.dtype, device=q.device)
+    else:
+        _require(out, "out", 4, q.device)
+        if out.dtype != q.dtype or tuple(out.shape) != (B, Hq, n, dv):
+            raise ValueError("out has the wrong shape or dtype")
+    check(lib.fa_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, n, m, d, dv,
+                     float(scale), 1 if causal else 0, _ptr(seq_lens), _stream(stream)))
+    return out
+
+
+def paged_decode_workspace_size(num_seqs, heads_q, heads_kv, dv, max_blocks_per_seq,
+                                block_size) -> int:
+    return int(load_library().fa_paged_decode_workspace_size(num_seqs, heads_q, heads_kv, dv,
+                                                            max_blocks_per_seq, block_size))
+
+
+def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | None = None,
+                 scale: float | None = None, out=None, workspace=None, stream=None):
+    """One query token per sequence over a paged cache.  q [S, Hq, d];
+    k_cache [NB, bs, Hkv, d]; v_cache [NB, bs, Hkv, dv]; block_table int32
+    [S, max_blocks]; seq_lens int32 [S].  scale defaults to 1/sqrt(d)."""
+    import torch
+    lib = load_library()
+    dev = q.device
+    _require(q, "q", 3, dev)
+    _require(k_cache, "k_cache", 4, dev)
+    _require(v_cache, "v_cache", 4, dev)
+    _require(block_table, "block_table", 2, dev)
+    _require(seq_lens, "seq_lens", 1, dev)
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache, v_cache must share a dtype")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    S, Hq, d = q.shape
+    NB, bs, Hkv, dk = k_cache.shape
+    dv = v_cache.shape[3]
+    if block_size is None:
+        block_size = bs
+    if bs != block_size or dk != d or tuple(v_cache.shape[:3]) != (NB, bs, Hkv):
+        raise ValueError("cache shapes do not match q / block_size")
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table / seq_lens batch mismatch")
+    maxb = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = paged_decode_workspace_size(S, Hq, Hkv, dv, maxb, block_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((S, Hq, dv), dtype=q.dtype, device=dev)
+    check(lib.fa_paged_decode(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv, d, dv,
+                              NB, maxb, float(scale), _ptr(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
