@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -38,6 +40,11 @@ struct BF16 {
   }
   static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
   static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+  // acc + lo(x) + hi(x) in one v_dot2 against (1, 1).
+  static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
 };
 
 struct F16 {
@@ -55,9 +62,31 @@ struct F16 {
   static __device__ __forceinline__ float hi(uint32_t x) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
   }
+  static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x),
+                                  __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
 };
 
+// The running max is raised lazily: only when a new tile's max exceeds it by
+// more than kSlack (log2 units).  Until then weights exp2(s - m) stay below
+// 2^kSlack = 256, which fp32 sums and bf16/fp16 operands hold comfortably, and
+// the rescale of the history (a multiply per accumulator) is skipped.
+constexpr float kSlack = 8.0f;
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // DPP lane moves within rows of 16 lanes (bound_ctrl: out-of-row reads give 0).
 template <int CTRL>
@@ -92,6 +121,15 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int total) {
   const int x = bid % kXcd, k = bid / kXcd;
   const int base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   return base + k;
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 }  // namespace fa

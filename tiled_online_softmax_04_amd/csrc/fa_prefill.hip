@@ -30,25 +30,37 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // MFMA kernel geometry
 // ---------------------------------------------------------------------------
-constexpr int kWaves = 4;
-constexpr int kBr = 32 * kWaves;  // query rows per workgroup
-constexpr int kBc = 64;           // keys per tile
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 8
+#endif
+#ifndef FA_PREFILL_QPW
+#define FA_PREFILL_QPW 32
+#endif
+constexpr int kWaves = FA_PREFILL_WAVES;    // waves per workgroup
+constexpr int kQPerWave = FA_PREFILL_QPW;   // queries per wave (32-column MFMA tiles)
+constexpr int kNT = kQPerWave / 32;         // query tiles per wave
+constexpr int kBr = kQPerWave * kWaves;     // query rows per workgroup
+constexpr int kBc = 64;                     // keys per tile
 constexpr int kThreads = 64 * kWaves;
+#ifndef FA_PREFILL_STAGES
+#define FA_PREFILL_STAGES 3
+#endif
+// LDS ring of K/V tiles: tile t is computed while tiles t+1 .. t+kStages-1 land.
+constexpr int kStages = FA_PREFILL_STAGES;
+static_assert(kStages == 2 || kStages == 3, "ring depth");
 
 template <int D>
 struct Geo {
-  static constexpr int kStride = D + 8;            // K tile row stride (elements), 16 B pad
-  static constexpr int kVtStride = kBc + 8;        // V^T tile row stride (elements)
-  static constexpr int kKElems = kBc * kStride;
-  static constexpr int kVtElems = D * kVtStride;
-  static constexpr int kStage = kKElems + kVtElems;  // elements per LDS stage
-  static constexpr int kChunks = D / 8;            // 16-byte chunks per row
-  static constexpr int kKRowsPerPass = kThreads / kChunks;
-  static constexpr int kKPasses = kBc / kKRowsPerPass;  // K chunks per thread
-  static constexpr int kVKeys = D / 32;            // consecutive keys per thread (V^T)
-  static constexpr int kVGroups = kBc / kVKeys;    // key groups per tile
-  static constexpr int kQSteps = D / 16;           // k-steps of S^T = K Q^T
-  static constexpr int kOTiles = D / 32;           // 32-row tiles of O^T
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int kTileElems = kBc * D;             // one K (or V) tile
+  static constexpr int kStageElems = 2 * kTileElems;     // K then V
+  static constexpr int kRowsPerDma = 64 / kChunks;       // rows one wave-wide DMA covers
+  static constexpr int kDmaPerTile = kBc / kRowsPerDma;  // wave DMAs per K (or V) tile
+  static constexpr int kDmaPerWave = 2 * kDmaPerTile / kWaves;
+  static_assert(2 * kDmaPerTile % kWaves == 0 && kDmaPerTile % kDmaPerWave == 0,
+                "each wave's DMAs must stay within the K or the V tile");
+  static constexpr int kQSteps = D / 16;                 // k-steps of S^T = K Q^T
+  static constexpr int kOTiles = D / 32;                 // 32-row tiles of O^T
 };
 
 // Row placement of the K tile inside each 32-row block.  The accumulator of a
@@ -61,8 +73,70 @@ __device__ __forceinline__ int kappa(int r) {
   return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 0xC);
 }
 
+// XOR swizzles of the 16-byte chunks of a row, so that the MFMA operand reads
+// hit distinct LDS banks: K rows (8 lanes read 8 rows at one chunk) and V rows
+// (16 lanes of a transposing read take 4 rows x 2 chunks).
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// Raw buffer descriptor over [base, base + bytes).  Loads at offsets outside
+// the range (including "negative" offsets, which wrap past 2^31) return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16 bytes per lane straight from a buffer into LDS: the wave's 64 lanes fill
+// 1 KB at `lds_base` in lane order (lane l at lds_base + 16*l).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// Transposing LDS read: within each 16 lanes, lane 4r+t names row r, columns
+// 4t..4t+3; lane c receives column c of the 4 rows.  Issued from inline asm so
+// that the byte offset OFF lands in the instruction's offset field; the result
+// is valid only after wait_lgkm0() followed by reg_barrier() on it.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF)
+               : "memory");
+  return r;
+}
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt untouched).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Make x look redefined here, so no use of x is scheduled above this point.
+template <class X>
+__device__ __forceinline__ void reg_barrier(X& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// s_waitcnt with vmcnt <= VM and lgkmcnt == 0 (expcnt untouched).
+template <int VM>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
+}
+
+// Workgroup barrier without a memory fence: the caller has already waited for
+// its own LDS traffic; the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <class T, int D, bool CAUSAL, bool RAGGED>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma(
+#ifndef FA_PREFILL_WAVES_PER_EU
+#define FA_PREFILL_WAVES_PER_EU (kWaves / 4)
+#endif
+__global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, const int32_t* __restrict__ seq_lens,
     int Hq, int group, int n, int m, int q_tiles, int total, float c) {
@@ -70,7 +144,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma(
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int ql = lane & 31, hf = lane >> 5;
 
   const int logical = xcd_contiguous(blockIdx.x, total);
@@ -90,183 +165,265 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma(
   uint16_t* Oh = O + q_base;
 
   // Padding rows of a left-padded sequence; out-of-range lengths are clamped.
-  const int pad = RAGGED ? min(max(n - seq_lens[b], 0), n) : 0;
+  const int pad =
+      RAGGED ? __builtin_amdgcn_readfirstlane(min(max(n - seq_lens[b], 0), n)) : 0;
   const int wg_q0 = qt * kBr;
   const int wg_q1 = min(n, wg_q0 + kBr);
-  const int wq0 = wg_q0 + w * 32;  // first query of this wave
-  const int qrow = wq0 + ql;       // this lane's query
-  // Rows that hold no real query: past n, or inside the left pad.
-  const bool q_ok = qrow < n && qrow >= pad;
+  const int wq0 = wg_q0 + w * kQPerWave;  // first query of this wave
+  int qrow[kNT];
+  bool q_ok[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    qrow[nt] = wq0 + 32 * nt + ql;
+    // Rows that hold no real query: past n, or inside the left pad.
+    q_ok[nt] = qrow[nt] < n && qrow[nt] >= pad;
+  }
 
   // Key range of this workgroup, in whole tiles.
   const int kv_begin = RAGGED ? (pad / kBc) * kBc : 0;
   const int kv_end = CAUSAL ? min(m, wg_q1) : m;
   const int t_begin = kv_begin / kBc;
   const int t_end = (RAGGED && wg_q1 <= pad) ? t_begin : (kv_end + kBc - 1) / kBc;
+  const int key_lo = RAGGED ? pad : 0;
+
+  // K and V of this head as buffers that start at the first valid key: rows
+  // before it (padding) and from m on read back as zeros, so no tile ever
+  // needs clamping and padding contents never reach the arithmetic.
+  const uint32_t kv_bytes = (uint32_t)(m - key_lo) * (uint32_t)(D * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(Kh + (size_t)key_lo * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(Vh + (size_t)key_lo * D, kv_bytes);
+
+  // DMA of a tile into a ring stage.  Lane l of a wave DMA fills LDS row
+  // p = first + l / kChunks, physical chunk l % kChunks, and fetches the key
+  // and logical chunk that belong there (kappa rows for K, swizzled chunks for
+  // both).  The per-lane byte offsets within a tile never change.
+  uint32_t dma_off[G::kDmaPerWave];
+  const bool dma_v = w * G::kDmaPerWave >= G::kDmaPerTile;  // first half of the waves: K
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    const int ii = w * G::kDmaPerWave + i - (dma_v ? G::kDmaPerTile : 0);
+    const int p = ii * G::kRowsPerDma + lane / G::kChunks;
+    const int pc = lane % G::kChunks;
+    const int klocal = dma_v ? p : ((p & ~31) | kappa(p & 31));
+    const int chunk = pc ^ (dma_v ? v_swz(p) : k_swz(p));
+    dma_off[i] = (uint32_t)(klocal * D + chunk * 8) * 2u;
+  }
+  const __amdgpu_buffer_rsrc_t rsrc_dma = dma_v ? rsrc_v : rsrc_k;
+  lds_char* const lds = (lds_char*)smem;
+  const int dma_lds0 = (dma_v ? G::kTileElems : 0) * 2 +
+                       (w * G::kDmaPerWave - (dma_v ? G::kDmaPerTile : 0)) *
+                           G::kRowsPerDma * D * 2;
+  auto issue_tile = [&](int t, int st) {
+    const uint32_t tile_off = (uint32_t)((t * kBc - key_lo) * D * 2);
+    lds_char* dst = lds + st * G::kStageElems * 2 + dma_lds0;
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i)
+      dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D * 2);
+  };
+
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (t_begin + i < t_end) issue_tile(t_begin + i, i);
 
   // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive d.
-  u32x4 qT[G::kQSteps];
+  u32x4 qT[kNT][G::kQSteps];
 #pragma unroll
-  for (int ks = 0; ks < G::kQSteps; ++ks) {
-    qT[ks] = q_ok ? load16(Qh + (size_t)qrow * D + ks * 16 + hf * 8) : u32x4{0, 0, 0, 0};
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < G::kQSteps; ++ks)
+      qT[nt][ks] = q_ok[nt] ? load16(Qh + (size_t)qrow[nt] * D + ks * 16 + hf * 8)
+                            : u32x4{0, 0, 0, 0};
+
+  f32x16 acc[G::kOTiles][kNT];
+  float m_run[kNT], l_run[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+#pragma unroll
+    for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] = f32x16{};
+    m_run[nt] = kSentinel;  // running max (scaled log2 units)
+    l_run[nt] = 0.f;        // this lane's half of the running sum
   }
 
-  f32x16 acc[G::kOTiles];
+  // Per-lane LDS byte offsets of the MFMA operands within a stage.
+  uint32_t k_off[G::kQSteps];  // K rows ql (and +32) for each k-step
 #pragma unroll
-  for (int t = 0; t < G::kOTiles; ++t) acc[t] = f32x16{};
-  float m_run = kSentinel;  // running max (scaled log2 units), finite start
-  float l_run = 0.f;        // this lane's half of the running sum
-
-  // -------- staging: global -> registers -> LDS --------
-  const int kc = tid % G::kChunks, kr0 = tid / G::kChunks;
-  const int vg = tid % G::kVGroups, vc = tid / G::kVGroups;
-  u32x4 kreg[G::kKPasses];
-  u32x4 vreg[G::kVKeys];
-
-  auto key_valid = [&](int key) { return key < m && (!RAGGED || key >= pad); };
-  auto load_tile = [&](int t) {
-    const int j0 = t * kBc;
+  for (int ks = 0; ks < G::kQSteps; ++ks)
+    k_off[ks] = (uint32_t)(ql * D + (((2 * ks + hf) ^ k_swz(ql)) * 8)) * 2u;
+  uint32_t v_off[G::kOTiles];  // transposing V reads, k-step 0, first half
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int key = 8 * (g >> 1) + (i >> 2);
+    const int chunk = 2 * (g & 1) + ((i & 3) >> 1);
 #pragma unroll
-    for (int p = 0; p < G::kKPasses; ++p) {
-      const int key = j0 + kr0 + p * G::kKRowsPerPass;
-      kreg[p] = key_valid(key) ? load16(Kh + (size_t)key * D + kc * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int r = 0; r < G::kVKeys; ++r) {
-      const int key = j0 + vg * G::kVKeys + r;
-      vreg[r] = key_valid(key) ? load16(Vh + (size_t)key * D + vc * 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks_ = smem + buf * G::kStage;
-    uint16_t* vt_ = ks_ + G::kKElems;
-#pragma unroll
-    for (int p = 0; p < G::kKPasses; ++p) {
-      const int r = kr0 + p * G::kKRowsPerPass;
-      const int row = (r & ~31) | kappa(r & 31);
-      store16(ks_ + row * G::kStride + kc * 8, kreg[p]);
-    }
-    // Transpose: element e of the 8 d-values of each of kVKeys keys goes to
-    // V^T row vc*8+e, columns vg*kVKeys .. +kVKeys.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint32_t wv[G::kVKeys / 2];
-#pragma unroll
-      for (int r2 = 0; r2 < G::kVKeys / 2; ++r2) {
-        const uint32_t a = vreg[2 * r2][e >> 1], bb = vreg[2 * r2 + 1][e >> 1];
-        wv[r2] = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u)) : ((a & 0xffffu) | (bb << 16));
-      }
-      uint16_t* dst = vt_ + (vc * 8 + e) * G::kVtStride + vg * G::kVKeys;
-      if constexpr (G::kVKeys == 4) {
-        *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = wv[0];
-      }
-    }
-  };
-
-  if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
+    for (int t2 = 0; t2 < G::kOTiles; ++t2)
+      v_off[t2] = (uint32_t)(key * D + (((4 * t2 + chunk) ^ v_swz(key)) * 8) + (i & 1) * 4) * 2u;
   }
-  __syncthreads();
+
+  wait_vm_lgkm0<0>();
+  bare_barrier();
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) load_tile(t + 1);
+    const int it = t - t_begin;
+    const int st = it % kStages;
+    // Refill the stage read in the previous iteration with tile t+kStages-1.
+    const bool pre = t + kStages - 1 < t_end;
+    if (pre) issue_tile(t + kStages - 1, (it + kStages - 1) % kStages);
 
     const int j0 = t * kBc;
     // Whole wave above the causal diagonal, or wholly padding: nothing to add.
-    const bool wave_idle = (CAUSAL && j0 > wq0 + 31) || (RAGGED && wq0 + 31 < pad);
+    const bool wave_idle = (CAUSAL && j0 > wq0 + kQPerWave - 1) ||
+                           (RAGGED && wq0 + kQPerWave - 1 < pad);
     if (!wave_idle) {
-      const uint16_t* ks_ = smem + buf * G::kStage;
-      const uint16_t* vt_ = ks_ + G::kKElems;
+      const lds_char* Ks = lds + st * G::kStageElems * 2;
+      const lds_char* Vs = Ks + G::kTileElems * 2;
 
-      // S^T[key][query] for 64 keys (two 32-row tiles) x 32 queries.
-      f32x16 st0 = f32x16{}, st1 = f32x16{};
+      // S^T[key][query]: 64 keys (two 32-row tiles) x kQPerWave queries.
+      f32x16 sacc[2][kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) sacc[0][nt] = sacc[1][nt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < G::kQSteps; ++ks) {
-        const u32x4 a0 = load16(ks_ + ql * G::kStride + ks * 16 + hf * 8);
-        const u32x4 a1 = load16(ks_ + (32 + ql) * G::kStride + ks * 16 + hf * 8);
-        st0 = T::mfma32x32x16(a0, qT[ks], st0);
-        st1 = T::mfma32x32x16(a1, qT[ks], st1);
+        const u32x4 a0 = *(const lds_u32x4*)(Ks + k_off[ks]);
+        const u32x4 a1 = *(const lds_u32x4*)(Ks + k_off[ks] + 32 * D * 2);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          sacc[0][nt] = T::mfma32x32x16(a0, qT[nt][ks], sacc[0][nt]);
+          sacc[1][nt] = T::mfma32x32x16(a1, qT[nt][ks], sacc[1][nt]);
+        }
       }
 
-      // Mask only tiles that straddle the diagonal, the pad or the end of K.
+      // V^T operands through transposing reads: 2 reads per (k-step j, dv tile).
+      const uint32_t vs_addr = (uint32_t)(uintptr_t)Vs;
+      uint32_t va[G::kOTiles];
+#pragma unroll
+      for (int t2 = 0; t2 < G::kOTiles; ++t2) va[t2] = vs_addr + v_off[t2];
+      u32x2 vr[4][G::kOTiles][2];
+      auto issue_v = [&](auto J) {
+        constexpr int j = decltype(J)::value;
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+          vr[j][t2][0] = ds_read_tr16_at<(16 * j) * D * 2>(va[t2]);
+          vr[j][t2][1] = ds_read_tr16_at<(16 * j + 4) * D * 2>(va[t2]);
+        }
+      };
+      auto mma_v = [&](auto J, const u32x4 (&pbr)[kNT][4]) {
+        constexpr int j = decltype(J)::value;
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+          reg_barrier(vr[j][t2][0]);
+          reg_barrier(vr[j][t2][1]);
+          const u32x4 a = {vr[j][t2][0][0], vr[j][t2][0][1], vr[j][t2][1][0], vr[j][t2][1][1]};
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) acc[t2][nt] = T::mfma32x32x16(a, pbr[nt][j], acc[t2][nt]);
+        }
+      };
+      static_for<0, 2>([&](auto J) { issue_v(J); });
+
+      // Mask only tiles that straddle the diagonal, the pad or the end of K
+      // (a real branch: most tiles need no mask at all).
       const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0) || (j0 + kBc > m) ||
                              (RAGGED && j0 < pad);
-      if (need_mask) {
+      if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kk = 16 * (i >> 3) + 8 * hf + (i & 7);
-          const int key0 = j0 + kk, key1 = j0 + 32 + kk;
-          const bool bad0 = (CAUSAL && key0 > qrow) || key0 >= m || (RAGGED && key0 < pad);
-          const bool bad1 = (CAUSAL && key1 > qrow) || key1 >= m || (RAGGED && key1 < pad);
-          st0[i] = bad0 ? -__builtin_inff() : st0[i];
-          st1[i] = bad1 ? -__builtin_inff() : st1[i];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            const int key = j0 + 32 * mt + kk;
+            const bool kbad = key >= m || (RAGGED && key < pad);
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) {
+              const bool bad = kbad || (CAUSAL && key > qrow[nt]);
+              sacc[mt][nt][i] = bad ? -__builtin_inff() : sacc[mt][nt][i];
+            }
+          }
         }
       }
 
-      // Online softmax: tile row max (lane-local + partner lane 32 away).
-      float mx = st0[0];
+      // Online softmax: tile row max (lane-local + the partner lane 32 away).
+      float mx[kNT];
+      bool raise = false;
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, st0[i]);
+      for (int nt = 0; nt < kNT; ++nt) {
+        float a = fmaxf(sacc[0][nt][0], sacc[0][nt][1]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st1[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-
-      // p = exp2(S*c - m) as the B operand of O^T += V^T P^T.
-      u32x4 pb[4];
-      float psum = 0.f;
+        for (int i = 2; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[0][nt][i], sacc[0][nt][i + 1]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int i = 0; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[1][nt][i], sacc[1][nt][i + 1]));
+        mx[nt] = max_xor32(a) * c;
+        raise = raise || mx[nt] > m_run[nt] + kSlack;
+      }
+      // Raise the running max only when the tile beats it by more than kSlack
+      // (wave-uniform branch).  Weights are then at most 2^kSlack, and acc and
+      // l always share the same m, so O = acc / l is unchanged.
+      if (__any(raise)) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 8 * (j & 1) + 2 * e;
-          const float s0 = (j < 2) ? st0[i] : st1[i];
-          const float s1 = (j < 2) ? st0[i + 1] : st1[i + 1];
-          const float p0 = fast_exp2(fmaf(s0, c, -m_new));
-          const float p1 = fast_exp2(fmaf(s1, c, -m_new));
-          psum += p0 + p1;
-          pb[j][e] = T::pack(p0, p1);
+        for (int nt = 0; nt < kNT; ++nt) {
+          const float m_new = fmaxf(m_run[nt], mx[nt]);
+          const float alpha = fast_exp2(m_run[nt] - m_new);
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] *= alpha;
+          m_run[nt] = m_new;
         }
       }
-      l_run = fmaf(l_run, alpha, psum);
 
+      // p = exp2(S*c - m) as the B operand of O^T += V^T P^T.  The running
+      // sum adds the same rounded weights the MFMA uses (two per v_dot2).
+      u32x4 pb[kNT][4];
 #pragma unroll
-      for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2] *= alpha;
-
+      for (int nt = 0; nt < kNT; ++nt) {
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-          const u32x4 a = load16(vt_ + (32 * t2 + ql) * G::kVtStride + 16 * j + 8 * hf);
-          acc[t2] = T::mfma32x32x16(a, pb[j], acc[t2]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 8 * (j & 1) + 2 * e;
+            const float p0 = fast_exp2(fmaf(sacc[j >> 1][nt][i], c, -m_run[nt]));
+            const float p1 = fast_exp2(fmaf(sacc[j >> 1][nt][i + 1], c, -m_run[nt]));
+            pb[nt][j][e] = T::pack(p0, p1);
+            if (e & 1) ps1 = T::add_pair(pb[nt][j][e], ps1);
+            else ps0 = T::add_pair(pb[nt][j][e], ps0);
+          }
         }
+        l_run[nt] += ps0 + ps1;
       }
+
+      // O^T += V^T P^T.  k-steps 0, 1 of V^T were requested before the
+      // softmax; 2, 3 go out now and land during the first half of the MFMAs.
+      static_for<2, 4>([&](auto J) { issue_v(J); });
+      wait_lgkm0();
+      static_for<0, 2>([&](auto J) { mma_v(J, pb); });
+      wait_lgkm0();
+      static_for<2, 4>([&](auto J) { mma_v(J, pb); });
     }
 
-    if (more) store_tile(buf ^ 1);
-    __syncthreads();
+    // This wave's part of tile t+1 has landed and its reads of stage st are
+    // done; after the barrier every wave may read t+1 and refill stage st.
+    if (kStages == 3 && pre) {
+      wait_vm_lgkm0<(kStages - 2) * G::kDmaPerWave>();  // tile t+2 may stay in flight
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    bare_barrier();
   }
 
   // -------- epilogue: O = acc / l, zero for rows without keys --------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = (l_tot > 0.f && q_ok) ? 1.f / l_tot : 0.f;
-  if (qrow < n && qrow >= wg_q0) {
-    uint16_t* orow = Oh + (size_t)qrow * D;
 #pragma unroll
-    for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+  for (int nt = 0; nt < kNT; ++nt) {
+    const float l_tot = sum_xor32(l_run[nt]);
+    const float inv = (l_tot > 0.f && q_ok[nt]) ? 1.f / l_tot : 0.f;
+    if (qrow[nt] < n) {
+      uint16_t* orow = Oh + (size_t)qrow[nt] * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dv0 = 32 * t2 + 8 * g + 4 * hf;
-        const uint32_t lo = T::pack(acc[t2][4 * g] * inv, acc[t2][4 * g + 1] * inv);
-        const uint32_t hi = T::pack(acc[t2][4 * g + 2] * inv, acc[t2][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + dv0) = u32x2{lo, hi};
+      for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dv0 = 32 * t2 + 8 * g + 4 * hf;
+          const uint32_t lo = T::pack(acc[t2][nt][4 * g] * inv, acc[t2][nt][4 * g + 1] * inv);
+          const uint32_t hi = T::pack(acc[t2][nt][4 * g + 2] * inv, acc[t2][nt][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + dv0) = u32x2{lo, hi};
+        }
       }
     }
   }
@@ -379,7 +536,7 @@ static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
   const int q_tiles = (a.n + kBr - 1) / kBr;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
-  const size_t lds = 2 * G::kStage * sizeof(uint16_t);
+  const size_t lds = kStages * G::kStageElems * sizeof(uint16_t);
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
