@@ -40,10 +40,14 @@ struct BF16 {
   }
   static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
   static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-  // acc + lo(x) + hi(x) in one v_dot2 against (1, 1).
+  // acc + lo(a)*lo(b) + hi(a)*hi(b) in one v_dot2_f32_bf16.
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+  }
+  // acc + lo(x) + hi(x): a v_dot2 against (1, 1).
   static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x),
-                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+    return dot2(x, 0x3F803F80u, acc);
   }
 };
 
@@ -62,9 +66,12 @@ struct F16 {
   static __device__ __forceinline__ float hi(uint32_t x) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
   }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
+  }
   static __device__ __forceinline__ float add_pair(uint32_t x, float acc) {
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x),
-                                  __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+    return dot2(x, 0x3C003C00u, acc);
   }
 };
 
@@ -87,6 +94,17 @@ __device__ __forceinline__ float sum_xor32(float x) {
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// sum of x over lanes l and l ^ 16 (v_permlane16_swap).
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // DPP lane moves within rows of 16 lanes (bound_ctrl: out-of-row reads give 0).
 template <int CTRL>
@@ -98,6 +116,11 @@ constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
 constexpr int kRowRor8 = 0x128;      // lane i <- lane (i+8) mod 16 within a row
+constexpr int kRowMirror = 0x140;    // lane i <- lane 15-i within a row
+
+// Sum / max over lanes l and l ^ 8 (a rotation by 8 inside each row of 16).
+__device__ __forceinline__ float sum_xor8(float x) { return x + dpp<kRowRor8>(x); }
+__device__ __forceinline__ float max_xor8(float x) { return fmaxf(x, dpp<kRowRor8>(x)); }
 
 // Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
 __device__ __forceinline__ float sum8(float x) {
@@ -106,6 +129,8 @@ __device__ __forceinline__ float sum8(float x) {
   x += dpp<kRowHalfMirror>(x);
   return x;
 }
+// Sum over each aligned group of 16 lanes (a DPP row).
+__device__ __forceinline__ float sum16(float x) { return sum8(x) + dpp<kRowMirror>(sum8(x)); }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -14,12 +14,20 @@
 // VGPRs and does the arithmetic on the vector ALUs.
 //
 // Lane layout of the split kernel: a wave takes 16 consecutive tokens at a
-// time; lane = 8 * slot + sub, token slot `slot` (0..7) handles tokens slot and
-// slot + 8 of the chunk, and `sub` (0..7) handles the 16-byte chunks sub and
-// sub + 8 of each row (D = 128; D = 64 has one chunk per lane).  A dot product
-// is finished by a sum over the 8 lanes of a slot (DPP).  The running max of a
-// head is kept uniform across the wave, so the rescale of the history is a
-// wave-uniform branch taken only when the max moves.
+// time.  Each lane owns one 16-byte column chunk of a row (kLpt = d/8 lanes
+// cover a 256- or 128-byte row) for kTpl tokens of the chunk: lane =
+// kLpt * slot + sub handles tokens slot, slot + kSlots, ... and chunk sub, so
+// one load instruction reads kSlots whole rows.
+//  - q.k: v_dot2 on packed 16-bit pairs, finished by a DPP sum over the kLpt
+//    lanes of a token;
+//  - p.v: the tokens of a lane are paired, so one v_dot2 adds
+//    p(t0) v(t0) + p(t1) v(t1) for one column (p rounded to the input type,
+//    as the prefill's P.V MFMA does, and l sums the same rounded values);
+//  - the running max is wave-uniform and raised only when some score beats it
+//    by more than kSlack (a wave vote), so the common path has no cross-lane
+//    max at all;
+//  - the next chunk's K/V loads are in flight while the current one is used,
+//    and the split's block-table entries are staged in LDS once.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -28,25 +36,60 @@ namespace fa {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecChunk = 16;  // tokens per wave step
+constexpr int kDecChunk = 16;          // tokens per wave step
+#ifndef FA_DECODE_SPLIT
+#define FA_DECODE_SPLIT 512
+#endif
+#ifndef FA_DECODE_WAVES_PER_EU
+#define FA_DECODE_WAVES_PER_EU 3
+#endif
+constexpr int kMaxSplitTokens = FA_DECODE_SPLIT;  // split sizes: powers of two up to this
+constexpr int kMaxSplitBlocks = kMaxSplitTokens + 1;
+
+template <int D>
+struct DecGeo {
+  static constexpr int kLpt = D / 8;              // lanes per token row
+  static constexpr int kSlots = 64 / kLpt;        // token slots per wave
+  static constexpr int kTpl = kDecChunk / kSlots; // tokens per lane per chunk
+  static_assert(kTpl % 2 == 0, "tokens of a lane are paired");
+};
+
+template <int LPT>
+__device__ __forceinline__ float sum_row(float x) {
+  if constexpr (LPT == 16) return sum16(x);
+  else return sum8(x);
+}
+// Sum / max over the token slots of a wave (lanes that share `sub`).
+template <int LPT>
+__device__ __forceinline__ float sum_slots(float x) {
+  if constexpr (LPT == 8) x = sum_xor8(x);
+  return sum_xor32(sum_xor16(x));
+}
+template <int LPT>
+__device__ __forceinline__ float max_slots(float x) {
+  if constexpr (LPT == 8) x = max_xor8(x);
+  return max_xor32(max_xor16(x));
+}
 
 template <class T, int D, int GW>
-__global__ __launch_bounds__(kDecThreads) void fa_decode_split(
+__global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode_split(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int bs, int Hq, int Hkv, int group, int subgroups,
     int maxb, int num_blocks, int split_tokens, int max_splits, float c,
-    float* __restrict__ part_m,
-    float* __restrict__ part_l, float* __restrict__ part_acc) {
-  constexpr int NCH = D / 64;     // 16-byte chunks per lane per row
-  constexpr int NE = NCH * 8;     // elements per lane per row
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_acc) {
+  using G = DecGeo<D>;
+  constexpr int TPL = G::kTpl;
+  __shared__ int bt_s[kMaxSplitBlocks];
   __shared__ float red_m[kDecWaves][GW];
   __shared__ float red_l[kDecWaves][GW];
   __shared__ float red_acc[kDecWaves][GW][D];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / subgroups;
-  const int sg = blockIdx.y % subgroups;
+  // KV heads (and head subgroups) vary fastest across workgroup ids, so the
+  // workgroups reading the rows of one cache block run side by side.
+  const int split = blockIdx.y;
+  const int kvh = blockIdx.x / subgroups;
+  const int sg = blockIdx.x % subgroups;
   const int seq = blockIdx.z;
   const int L = seq_lens[seq];
   const int tok0 = split * split_tokens;
@@ -54,134 +97,131 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split(
   const int tok1 = min(L, tok0 + split_tokens);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int slot = lane >> 3, sub = lane & 7;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = lane / G::kLpt, sub = lane % G::kLpt;
   const int h0 = kvh * group + sg * GW;  // first query head of this workgroup
 
-  // Query values at this lane's dims, float32.
-  float qf[GW][NE];
-#pragma unroll
-  for (int g = 0; g < GW; ++g) {
-    const uint16_t* qh = Q + ((size_t)seq * Hq + h0 + g) * D;
-#pragma unroll
-    for (int cc = 0; cc < NCH; ++cc) {
-      const u32x4 x = load16(qh + (sub + 8 * cc) * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[g][cc * 8 + 2 * e] = T::lo(x[e]);
-        qf[g][cc * 8 + 2 * e + 1] = T::hi(x[e]);
-      }
-    }
-  }
+  // Physical blocks of this split.  Entries and lengths outside their stated
+  // ranges are clamped so that no access leaves the buffers.
+  const int blk0 = tok0 / bs;
+  const int nblk = (tok1 - 1) / bs - blk0 + 1;
+  const int32_t* bt = block_table + (size_t)seq * maxb;
+  for (int i = tid; i < nblk; i += kDecThreads)
+    bt_s[i] = min(max(bt[min(blk0 + i, maxb - 1)], 0), num_blocks - 1);
 
-  float m_run[GW], l_run[GW], acc[GW][NE];
+  // Query values at this lane's 8 dims, packed 16-bit pairs.
+  u32x4 qp[GW];
+#pragma unroll
+  for (int g = 0; g < GW; ++g) qp[g] = load16(Q + ((size_t)seq * Hq + h0 + g) * D + sub * 8);
+
+  float m_run[GW], l_run[GW], acc[GW][8];
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
     m_run[g] = kSentinel;
     l_run[g] = 0.f;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) acc[g][e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
 
-  const int32_t* bt = block_table + (size_t)seq * maxb;
   const size_t row_stride = (size_t)Hkv * D;
-
-  for (int t0 = tok0 + w * kDecChunk; t0 < tok1; t0 += kDecWaves * kDecChunk) {
-    u32x4 kx[2][NCH], vx[2][NCH];
-    bool valid[2];
+  // K/V chunks of this lane's tokens in the 16-token chunk at t0.  Tokens
+  // past tok1 read a valid row (tok0) and are masked out of the softmax.
+  // The first chunks read their block ids from the table in global memory,
+  // so their loads need not wait for the staging of the table in LDS.
+  auto load_chunk = [&](int t0, u32x4 (&kx)[TPL], u32x4 (&vx)[TPL], bool from_lds) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int tok = t0 + slot + 8 * tt;
-      valid[tt] = tok < tok1;
-      const int tk = valid[tt] ? tok : tok0;
-      // Table entries and lengths outside their stated ranges are clamped so
-      // that no access leaves the buffers (the result is then unspecified).
-      const int phys = min(max(bt[min(tk / bs, maxb - 1)], 0), num_blocks - 1);
-      const size_t row = ((size_t)phys * bs + (tk % bs)) * row_stride + (size_t)kvh * D;
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-        kx[tt][cc] = valid[tt] ? load16(Kc + row + (sub + 8 * cc) * 8) : u32x4{0, 0, 0, 0};
-        vx[tt][cc] = valid[tt] ? load16(Vc + row + (sub + 8 * cc) * 8) : u32x4{0, 0, 0, 0};
-      }
+    for (int tt = 0; tt < TPL; ++tt) {
+      int tok = t0 + slot + G::kSlots * tt;
+      tok = tok < tok1 ? tok : tok0;
+      const int phys = from_lds ? bt_s[tok / bs - blk0]
+                                : min(max(bt[min(tok / bs, maxb - 1)], 0), num_blocks - 1);
+      const size_t off = ((size_t)phys * bs + (tok % bs)) * row_stride + (size_t)kvh * D + sub * 8;
+      kx[tt] = load16(Kc + off);
+      vx[tt] = load16(Vc + off);
     }
+  };
 
-    // scores of the two tokens for every head of the group
-    float s[GW][2];
+  // One chunk: scores, the lazy max, weights and the weighted sum of values.
+  auto consume = [&](int t0, const u32x4 (&kx)[TPL], const u32x4 (&vx)[TPL]) {
+    // scores of this lane's tokens for every head of the group
+    float s[GW][TPL];
+    bool raise = false;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float kf[NE];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[cc * 8 + 2 * e] = T::lo(kx[tt][cc][e]);
-          kf[cc * 8 + 2 * e + 1] = T::hi(kx[tt][cc][e]);
-        }
-      }
+    for (int tt = 0; tt < TPL; ++tt) {
+      const bool valid = t0 + slot + G::kSlots * tt < tok1;
 #pragma unroll
       for (int g = 0; g < GW; ++g) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < NE; ++e) a = fmaf(qf[g][e], kf[e], a);
-        a = sum8(a);
-        s[g][tt] = valid[tt] ? a * c : -__builtin_inff();
+        float a0 = T::dot2(qp[g][0], kx[tt][0], 0.f);
+        float a1 = T::dot2(qp[g][1], kx[tt][1], 0.f);
+        a0 = T::dot2(qp[g][2], kx[tt][2], a0);
+        a1 = T::dot2(qp[g][3], kx[tt][3], a1);
+        const float a = sum_row<G::kLpt>(a0 + a1);
+        s[g][tt] = valid ? a * c : -__builtin_inff();
+        raise = raise || s[g][tt] > m_run[g] + kSlack;
       }
     }
-
-    // wave-uniform running max per head
+    // Rare: raise the wave-uniform running max to the chunk max.
+    if (__any(raise)) {
 #pragma unroll
-    for (int g = 0; g < GW; ++g) {
-      float mx = fmaxf(s[g][0], s[g][1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 8));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (mx > m_run[g]) {
-        const float alpha = fast_exp2(m_run[g] - mx);
+      for (int g = 0; g < GW; ++g) {
+        float mx = s[g][0];
+#pragma unroll
+        for (int tt = 1; tt < TPL; ++tt) mx = fmaxf(mx, s[g][tt]);
+        mx = max_slots<G::kLpt>(mx);
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = fast_exp2(m_run[g] - m_new);
         l_run[g] *= alpha;
 #pragma unroll
-        for (int e = 0; e < NE; ++e) acc[g][e] *= alpha;
-        m_run[g] = mx;
+        for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+        m_run[g] = m_new;
       }
     }
-
-    // weights and the weighted sum of values
+    // weights of token pairs, packed, and the paired weighted sum of values
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float vf[NE];
-#pragma unroll
-      for (int cc = 0; cc < NCH; ++cc) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[cc * 8 + 2 * e] = T::lo(vx[tt][cc][e]);
-          vf[cc * 8 + 2 * e + 1] = T::hi(vx[tt][cc][e]);
-        }
-      }
+    for (int pr = 0; pr < TPL / 2; ++pr) {
+      uint32_t pp[GW];
 #pragma unroll
       for (int g = 0; g < GW; ++g) {
-        const float p = fast_exp2(s[g][tt] - m_run[g]);
-        l_run[g] += p;
+        pp[g] = T::pack(fast_exp2(s[g][2 * pr] - m_run[g]), fast_exp2(s[g][2 * pr + 1] - m_run[g]));
+        l_run[g] = T::add_pair(pp[g], l_run[g]);
+      }
 #pragma unroll
-        for (int e = 0; e < NE; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = vx[2 * pr][e], b = vx[2 * pr + 1][e];
+        const uint32_t lo = (a & 0xffffu) | (b << 16);      // column 2e of both tokens
+        const uint32_t hi = (a >> 16) | (b & 0xffff0000u);  // column 2e+1
+#pragma unroll
+        for (int g = 0; g < GW; ++g) {
+          acc[g][2 * e] = T::dot2(pp[g], lo, acc[g][2 * e]);
+          acc[g][2 * e + 1] = T::dot2(pp[g], hi, acc[g][2 * e + 1]);
+        }
       }
     }
+  };
+
+  // Two register buffers, two chunks in flight: chunk i+2 is requested as
+  // soon as chunk i has been consumed.  Chunks past tok1 load clamped rows
+  // and are fully masked.
+  constexpr int kStep = kDecWaves * kDecChunk;
+  u32x4 ka[TPL], va[TPL], kb[TPL], vb[TPL];
+  int t0 = tok0 + w * kDecChunk;
+  load_chunk(min(t0, tok1 - 1), ka, va, false);
+  load_chunk(min(t0 + kStep, tok1 - 1), kb, vb, false);
+  __syncthreads();  // block-table entries staged in LDS
+  for (; t0 < tok1; t0 += 2 * kStep) {
+    consume(t0, ka, va);
+    load_chunk(min(t0 + 2 * kStep, tok1 - 1), ka, va, true);
+    if (t0 + kStep < tok1) consume(t0 + kStep, kb, vb);
+    load_chunk(min(t0 + 3 * kStep, tok1 - 1), kb, vb, true);
   }
 
-  // Sum over the 8 token slots (lanes with equal `sub`); m is wave-uniform.
+  // Sum over the token slots (lanes sharing `sub`); m is wave-uniform.
 #pragma unroll
   for (int g = 0; g < GW; ++g) {
-    float l = l_run[g];
-    l += __shfl_xor(l, 8);
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    l_run[g] = l;
+    l_run[g] = sum_slots<G::kLpt>(l_run[g]);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      float x = acc[g][e];
-      x += __shfl_xor(x, 8);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[g][e] = x;
-    }
+    for (int e = 0; e < 8; ++e) acc[g][e] = sum_slots<G::kLpt>(acc[g][e]);
   }
   if (slot == 0) {
 #pragma unroll
@@ -191,9 +231,7 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split(
         red_l[w][g] = l_run[g];
       }
 #pragma unroll
-      for (int cc = 0; cc < NCH; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red_acc[w][g][(sub + 8 * cc) * 8 + e] = acc[g][cc * 8 + e];
+      for (int e = 0; e < 8; ++e) red_acc[w][g][sub * 8 + e] = acc[g][e];
     }
   }
   __syncthreads();
@@ -220,7 +258,9 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split(
   }
 }
 
-// One wave per (sequence, query head): merge the splits' (m, l, acc).
+// One wave per (sequence, query head): merge the splits' (m, l, acc).  Lane s
+// reads split s's (m, l); the weights 2^(m_s - M) are shared across the wave
+// and every lane sums its D/64 columns over the splits.
 template <class T, int D>
 __global__ __launch_bounds__(64) void fa_decode_merge(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
@@ -233,17 +273,30 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
   const int ns = min(max((L + split_tokens - 1) / split_tokens, 0), max_splits);
   const size_t base = ((size_t)seq * Hq + h) * max_splits;
 
-  float M = kSentinel;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part_m[base + s]);
-  float l = 0.f, a[PER];
+  // pass 1: the largest running max over all splits
+  float M = -__builtin_inff();
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_m[base + s]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  // pass 2: weights 2^(m_s - M), 64 splits at a time (one per lane)
+  float a[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) a[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = fast_exp2(part_m[base + s] - M);
-    l = fmaf(f, part_l[base + s], l);
+  float l = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + lane;
+    const float wgt = s < ns ? fast_exp2(part_m[base + s] - M) : 0.f;
+    if (s < ns) l = fmaf(wgt, part_l[base + s], l);
+    const int cnt = min(64, ns - s0);
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = __shfl(wgt, j);
+      const float* src = part_acc + (base + s0 + j) * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) a[e] = fmaf(f, part_acc[(base + s) * D + lane * PER + e], a[e]);
+      for (int e = 0; e < PER; ++e) a[e] = fmaf(wj, src[e], a[e]);
+    }
   }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   uint16_t* orow = O + ((size_t)seq * Hq + h) * D + lane * PER;
   if constexpr (PER == 2) {
@@ -264,8 +317,9 @@ DecodePlan decode_plan(int num_seqs, int heads_q, int heads_kv, int max_blocks_p
   p.heads_per_wg = (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1;
   p.subgroups = group / p.heads_per_wg;
   const long long max_tokens = (long long)max_blocks_per_seq * block_size;
-  // 512 keys per split; smaller when the batch alone cannot fill the GPU.
-  int st = 512;
+  // kMaxSplitTokens keys per split; smaller when the batch alone cannot fill
+  // the GPU with 2048 workgroups.
+  int st = kMaxSplitTokens;
   const long long base = (long long)num_seqs * heads_kv * p.subgroups;
   while (st > 64 && base * ((max_tokens + st - 1) / st) < 2048) st /= 2;
   p.split_tokens = st;
@@ -283,7 +337,7 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   float* part_l = part_m + (size_t)a.num_seqs * a.heads_q * p.max_splits;
   float* part_acc = part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits;
   const float c = a.scale * kLog2e;
-  dim3 grid1(p.max_splits, a.heads_kv * p.subgroups, a.num_seqs);
+  dim3 grid1(a.heads_kv * p.subgroups, p.max_splits, a.num_seqs);
   hipLaunchKernelGGL((fa_decode_split<T, D, GW>), grid1, dim3(kDecThreads), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
                      (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.block_size,

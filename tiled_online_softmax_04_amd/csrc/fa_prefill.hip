@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
             const float p1 = fast_exp2(fmaf(sacc[j >> 1][nt][i + 1], c, -m_run[nt]));
             pb[nt][j][e] = T::pack(p0, p1);
             if (e & 1) ps1 = T::add_pair(pb[nt][j][e], ps1);
-            else ps0 = T::add_pair(pb[nt][j][e], ps0);
+            else ps0 = T::add_pair(pb[nt][j][e], ps0);  // two chains for latency
           }
         }
         l_run[nt] += ps0 + ps1;
