@@ -98,8 +98,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU needs a few hundred calls to reach
-                         steady clocks")
+                    help="untimed steps first; the GPU needs a few hundred calls to "
+                         "reach steady clocks")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
