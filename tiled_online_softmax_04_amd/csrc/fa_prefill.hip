@@ -74,10 +74,19 @@ __device__ __forceinline__ int kappa(int r) {
 }
 
 // XOR swizzles of the 16-byte chunks of a row, so that the MFMA operand reads
-// hit distinct LDS banks: K rows (8 lanes read 8 rows at one chunk) and V rows
-// (16 lanes of a transposing read take 4 rows x 2 chunks).
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+// hit distinct banks of the 64-bank (256 bytes per cycle) LDS:
+//  - K: a 16-byte read serves 16 lanes per cycle, 16 rows at one logical
+//    chunk; rows are 256 B (d = 128: 16 chunks) or 128 B (d = 64: two rows
+//    share the bank width), so the XOR spreads 16 rows over 16 slots;
+//  - V: a transposing read serves 32 lanes per cycle, 4 rows x 4 chunks.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     const int p = ii * G::kRowsPerDma + lane / G::kChunks;
     const int pc = lane % G::kChunks;
     const int klocal = dma_v ? p : ((p & ~31) | kappa(p & 31));
-    const int chunk = pc ^ (dma_v ? v_swz(p) : k_swz(p));
+    const int chunk = pc ^ (dma_v ? v_swz<D>(p) : k_swz<D>(p));
     dma_off[i] = (uint32_t)(klocal * D + chunk * 8) * 2u;
   }
   const __amdgpu_buffer_rsrc_t rsrc_dma = dma_v ? rsrc_v : rsrc_k;
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   uint32_t k_off[G::kQSteps];  // K rows ql (and +32) for each k-step
 #pragma unroll
   for (int ks = 0; ks < G::kQSteps; ++ks)
-    k_off[ks] = (uint32_t)(ql * D + (((2 * ks + hf) ^ k_swz(ql)) * 8)) * 2u;
+    k_off[ks] = (uint32_t)(ql * D + (((2 * ks + hf) ^ k_swz<D>(ql)) * 8)) * 2u;
   uint32_t v_off[G::kOTiles];  // transposing V reads, k-step 0, first half
   {
     const int g = lane >> 4, i = lane & 15;
@@ -256,7 +265,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     const int chunk = 2 * (g & 1) + ((i & 3) >> 1);
 #pragma unroll
     for (int t2 = 0; t2 < G::kOTiles; ++t2)
-      v_off[t2] = (uint32_t)(key * D + (((4 * t2 + chunk) ^ v_swz(key)) * 8) + (i & 1) * 4) * 2u;
+      v_off[t2] = (uint32_t)(key * D + (((4 * t2 + chunk) ^ v_swz<D>(key)) * 8) + (i & 1) * 4) * 2u;
   }
 
   wait_vm_lgkm0<0>();
