@@ -121,7 +121,8 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int heads_q, int heads_kv, i
  * d in {64, 128}.
  * FA_ERR_INVALID: null pointers for non-empty work, non-positive block_size,
  *   num_blocks or max_blocks_per_seq, negative sizes, heads_q % heads_kv != 0,
- *   non-finite or non-positive scale, misaligned pointers.
+ *   non-finite or non-positive scale, misaligned pointers, a cache of 2^32 or
+ *   more token rows (num_blocks * block_size) or 2^40 or more elements.
  * FA_ERR_WORKSPACE: workspace_bytes below the required size (or a null workspace).
  * Two kernels are enqueued: the split pass and the merge pass.
  */

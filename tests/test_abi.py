@@ -105,6 +105,7 @@ def dec(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, 
     (dict(Hkv=0), fa.FA_ERR_INVALID),
     (dict(S=-2), fa.FA_ERR_INVALID),
     (dict(S=70000), fa.FA_ERR_INVALID),
+    (dict(NB=1 << 28, bs=16, Hkv=1, Hq=1, d=64, dv=64), fa.FA_ERR_INVALID),  # 2^32 rows
     (dict(scale=0.0), fa.FA_ERR_INVALID),
     (dict(d=80, dv=80), fa.FA_ERR_UNSUPPORTED),
     (dict(dt=0), fa.FA_ERR_UNSUPPORTED),

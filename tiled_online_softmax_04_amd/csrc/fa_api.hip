@@ -129,6 +129,8 @@ fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const
     return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
   if ((long long)num_blocks * block_size * heads_kv * d >= (1LL << 40))
     return fail(FA_ERR_INVALID, "cache larger than 2^40 elements");
+  if ((long long)num_blocks * block_size >= (1LL << 32))
+    return fail(FA_ERR_INVALID, "cache holds 2^32 or more token rows");
   if (dt == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "paged decode supports f16 and bf16");
   if (num_seqs == 0 || heads_q == 0) return FA_OK;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)

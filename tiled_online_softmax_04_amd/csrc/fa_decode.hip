@@ -71,11 +71,13 @@ __device__ __forceinline__ float max_slots(float x) {
   return max_xor32(max_xor16(x));
 }
 
-template <class T, int D, int GW>
+// POW2: block_size is 1 << bs_shift, so block and slot indices are a shift
+// and a mask rather than an integer division per token.
+template <class T, int D, int GW, bool POW2>
 __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode_split(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, int bs, int Hq, int Hkv, int group, int subgroups,
+    const int32_t* __restrict__ seq_lens, int bs, int bs_shift, int Hq, int Hkv, int group, int subgroups,
     int maxb, int num_blocks, int split_tokens, int max_splits, float c,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_acc) {
   using G = DecGeo<D>;
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
 
   // Physical blocks of this split.  Entries and lengths outside their stated
   // ranges are clamped so that no access leaves the buffers.
-  const int blk0 = tok0 / bs;
-  const int nblk = (tok1 - 1) / bs - blk0 + 1;
+  const int blk0 = POW2 ? tok0 >> bs_shift : tok0 / bs;
+  const int nblk = (POW2 ? (tok1 - 1) >> bs_shift : (tok1 - 1) / bs) - blk0 + 1;
   const int32_t* bt = block_table + (size_t)seq * maxb;
   for (int i = tid; i < nblk; i += kDecThreads)
     bt_s[i] = min(max(bt[min(blk0 + i, maxb - 1)], 0), num_blocks - 1);
@@ -134,9 +136,14 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
     for (int tt = 0; tt < TPL; ++tt) {
       int tok = t0 + slot + G::kSlots * tt;
       tok = tok < tok1 ? tok : tok0;
-      const int phys = from_lds ? bt_s[tok / bs - blk0]
-                                : min(max(bt[min(tok / bs, maxb - 1)], 0), num_blocks - 1);
-      const size_t off = ((size_t)phys * bs + (tok % bs)) * row_stride + (size_t)kvh * D + sub * 8;
+      const int blk = POW2 ? tok >> bs_shift : tok / bs;
+      const int in_blk = tok - blk * bs;
+      const int phys = from_lds ? bt_s[blk - blk0]
+                                : min(max(bt[min(blk, maxb - 1)], 0), num_blocks - 1);
+      // Row index of the token in the cache: fits 32 bits for any cache that
+      // fits in device memory.
+      const uint32_t row = (uint32_t)phys * (uint32_t)bs + (uint32_t)in_blk;
+      const size_t off = (size_t)row * row_stride + (size_t)(kvh * D + sub * 8);
       kx[tt] = load16(Kc + off);
       vx[tt] = load16(Vc + off);
     }
@@ -333,14 +340,18 @@ size_t decode_workspace_bytes(const DecodePlan& p, int num_seqs, int heads_q, in
 
 template <class T, int D, int GW>
 static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
+  const int bs = a.block_size;
+  const bool pow2 = (bs & (bs - 1)) == 0;
+  const int shift = pow2 ? __builtin_ctz((unsigned)bs) : -1;
   float* part_m = (float*)a.workspace;
   float* part_l = part_m + (size_t)a.num_seqs * a.heads_q * p.max_splits;
   float* part_acc = part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits;
   const float c = a.scale * kLog2e;
   dim3 grid1(a.heads_kv * p.subgroups, p.max_splits, a.num_seqs);
-  hipLaunchKernelGGL((fa_decode_split<T, D, GW>), grid1, dim3(kDecThreads), 0,
+  auto kernel = pow2 ? &fa_decode_split<T, D, GW, true> : &fa_decode_split<T, D, GW, false>;
+  hipLaunchKernelGGL(kernel, grid1, dim3(kDecThreads), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k_cache,
-                     (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, a.block_size,
+                     (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, bs, shift,
                      a.heads_q, a.heads_kv, a.heads_q / a.heads_kv, p.subgroups,
                      a.max_blocks_per_seq, a.num_blocks, p.split_tokens, p.max_splits, c, part_m,
                      part_l, part_acc);

@@ -1,15 +1,17 @@
 // Prefill attention kernels for gfx950 (CDNA4).
 //
-// fa_fwd_mfma: bf16 / fp16 inputs.  One workgroup of 4 waves owns 128 query
-// rows of one (batch, head); each wave owns 32 of them.  The wave keeps its
-// queries resident in VGPRs as MFMA operands ("Q 常驻片上寄存器", 10100.com
-// section 7) and streams 64-key K/V tiles through LDS (double-buffered, the
-// next tile's global loads in flight while the current one is computed).  Per
-// tile it forms S^T = K Q^T with v_mfma_f32_32x32x16, applies the online-softmax
-// update of the same section (running max, rescale of the history by
-// exp(m_old - m_new), running sum) and accumulates O^T += V^T P^T with a second
-// MFMA.  Tiles wholly above the causal diagonal or wholly inside a left pad are
-// never visited (10100.com section 6).
+// fa_fwd_mfma: bf16 / fp16 inputs.  One workgroup of 8 waves (two per SIMD)
+// owns 256 query rows of one (batch, head); each wave owns 32 of them and
+// keeps them resident in VGPRs as MFMA operands ("Q 常驻片上寄存器", 10100.com
+// section 7).  64-key K/V tiles stream through a ring of three LDS stages:
+// each wave moves its share of a tile with buffer loads that write LDS
+// directly (no VGPR round trip), two tiles ahead of the one being computed.
+// Per tile the wave forms S^T = K Q^T with v_mfma_f32_32x32x16, applies the
+// online-softmax update of the same section (running max, rescale of the
+// history by exp(m_old - m_new), running sum) and accumulates O^T += V^T P^T
+// with a second MFMA whose V^T operands come from transposing LDS reads.  Tiles
+// wholly above the causal diagonal or wholly inside a left pad are never
+// visited (10100.com section 6).
 //
 // Why S^T rather than S: in the 32x32 MFMA accumulator each lane holds one
 // column and 16 rows.  With keys as rows and queries as columns every lane
