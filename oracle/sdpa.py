@@ -19,6 +19,12 @@ What it computes (all arithmetic in float64 on exactly upcast inputs):
   as S12 recommends against exp(-inf - -inf).
 * ``merge_partials`` / ``split_key_attention`` -- combining (m, l, o) states
   of disjoint key ranges (S12 flash-decoding and exercise 1).
+* ``attention_range`` / ``merge_lse`` -- the definition restricted to a key
+  range, reported as the range's normalised output and the natural log of its
+  softmax denominator (log-sum-exp), and the merge of such pieces.  This is
+  the (m, l, o) state of S12's split over key ranges ("除了快，它还解锁了
+  什么": ring attention and flash-decoding exchange exactly these partial
+  states) written as (o, lse) with lse = m + log l.
 
 Readings of points the pages leave open:
 * scale is explicit; callers pass 1/sqrt(d) (10100.com section 2, S12) or 1
@@ -261,3 +267,66 @@ def split_key_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: floa
     parts = [online_partial(q, np.arange(n), k, v, scale, tile, lo, hi, causal, pad)
              for lo, hi in zip(bounds[:-1], bounds[1:])]
     return merge_partials(parts)
+
+
+# --------------------------------------------------------------------------
+# Key-range pieces and their merge (S12 split over key ranges, exercise 1)
+# --------------------------------------------------------------------------
+def attention_range(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                    causal: bool = False, pads=None, key_begin: int = 0, key_end=None):
+    """The definition over the allowed keys that also lie in [key_begin, key_end).
+
+    Returns (O [B, Hq, n, dv], lse [B, Hq, n]): O is the softmax-weighted mean
+    of those keys' values and lse = log(sum exp(s_ij)) over them, computed as
+    max + log(sum exp(s - max)).  A row with no such key has O = 0 and
+    lse = -inf.  Keys outside the range are never read.
+    """
+    B, Hq, n, _ = q.shape
+    Hkv, m = k.shape[1], k.shape[2]
+    group = Hq // Hkv
+    key_end = m if key_end is None else min(int(key_end), m)
+    out = np.zeros((B, Hq, n, v.shape[3]))
+    lse = np.full((B, Hq, n), -np.inf)
+    for b in range(B):
+        pad = 0 if pads is None else int(pads[b])
+        lo = max(int(key_begin), pad)
+        if lo >= key_end:
+            continue
+        key_idx = np.arange(lo, key_end, dtype=np.int64)
+        row_idx = np.arange(n, dtype=np.int64)
+        for h in range(Hq):
+            ks, vs = k[b, h // group, lo:key_end], v[b, h // group, lo:key_end]
+            s = scores(q[b, h], ks, scale)
+            ok = allowed_keys(row_idx, key_idx, causal, pad)
+            s = np.where(ok, s, -np.inf)
+            mx = s.max(axis=1)
+            has = np.isfinite(mx)
+            mx0 = np.where(has, mx, 0.0)
+            e = np.where(ok, np.exp(s - mx0[:, None]), 0.0)
+            den = e.sum(axis=1)
+            out[b, h] = np.where(has[:, None], (e @ vs) / np.where(has, den, 1.0)[:, None], 0.0)
+            lse[b, h] = np.where(has, mx0 + np.log(np.where(has, den, 1.0)), -np.inf)
+    return out, lse
+
+
+def merge_lse(parts):
+    """Merge (O_s, lse_s) pieces of disjoint key ranges into (O, lse).
+
+    With L = max_s lse_s and w_s = exp(lse_s - L): O = sum w_s O_s / sum w_s
+    and lse = L + log(sum w_s) -- the rescale of the recurrence applied to
+    whole pieces (S12 exercise 1), since O_s = acc_s / l_s and lse_s = m_s +
+    log l_s.  Pieces with lse_s = -inf weigh 0; if all are -inf, O = 0.
+    """
+    lses = np.stack([p_[1] for p_ in parts])
+    L = lses.max(axis=0)
+    has = np.isfinite(L)
+    L0 = np.where(has, L, 0.0)
+    w_tot = np.zeros_like(L0)
+    o_tot = np.zeros_like(parts[0][0], dtype=np.float64)
+    for o_s, lse_s in parts:
+        w = np.where(np.isfinite(lse_s), np.exp(np.where(np.isfinite(lse_s), lse_s, 0.0) - L0), 0.0)
+        w_tot = w_tot + w
+        o_tot = o_tot + w[..., None] * o_s
+    o = np.where(has[..., None], o_tot / np.where(has, w_tot, 1.0)[..., None], 0.0)
+    lse = np.where(has, L0 + np.log(np.where(has, w_tot, 1.0)), -np.inf)
+    return o, lse

@@ -225,10 +225,93 @@ def pin_paged_equals_contiguous():
     return worst <= TIGHT
 
 
+# --------------------------------------------------------------------------
+# key-range pieces (o, lse) and their merge
+# --------------------------------------------------------------------------
+def brute_force_range(q, k, v, scale, lo, hi, causal=False, pad=0):
+    """Literal loops: the allowed keys of row i inside [lo, hi), their
+    weighted mean of values and log(sum exp(score))."""
+    n, d = q.shape
+    dv = v.shape[1]
+    out, lse = np.zeros((n, dv)), np.full(n, -np.inf)
+    for i in range(n):
+        allowed = [j for j in range(max(lo, pad), hi)
+                   if (not causal or j <= i) and i >= pad]
+        if not allowed:
+            continue
+        sc = {j: sum(float(q[i, t]) * float(k[j, t]) for t in range(d)) * scale for j in allowed}
+        w = {j: math.exp(sc[j]) for j in allowed}
+        tot = sum(w.values())
+        lse[i] = math.log(tot)
+        for j in allowed:
+            for c in range(dv):
+                out[i, c] += w[j] / tot * float(v[j, c])
+    return out, lse
+
+
+def pin_range_bruteforce():
+    rng = np.random.default_rng(21)
+    worst = 0.0
+    for causal, pad, lo, hi in [(False, 0, 0, 9), (False, 0, 3, 7), (True, 0, 2, 9),
+                                (True, 3, 0, 5), (False, 2, 6, 6), (True, 0, 8, 9)]:
+        n = m = 9
+        q, k, v = rnd(rng, n, 4), rnd(rng, m, 4), rnd(rng, m, 3)
+        got_o, got_l = oracle.attention_range(q[None, None], k[None, None], v[None, None], 0.6,
+                                              causal, None if pad == 0 else [pad], lo, hi)
+        ref_o, ref_l = brute_force_range(q, k, v, 0.6, lo, hi, causal, pad)
+        if not np.array_equal(np.isinf(got_l[0, 0]), np.isinf(ref_l)):
+            return False
+        fin = np.isfinite(ref_l)
+        worst = max(worst, np.abs(got_o[0, 0] - ref_o).max(),
+                    np.abs(got_l[0, 0][fin] - ref_l[fin]).max(initial=0.0))
+    return worst <= TIGHT
+
+
+def pin_range_merge():
+    rng = np.random.default_rng(22)
+    worst = 0.0
+    for causal, pads in [(False, None), (True, None), (True, [0, 5])]:
+        B, Hq, Hkv, n, d = 2, 4, 2, 20, 6
+        q = rnd(rng, B, Hq, n, d, scale=2.0)
+        k, v = rnd(rng, B, Hkv, n, d, scale=2.0), rnd(rng, B, Hkv, n, d)
+        cuts = np.sort(rng.integers(0, n + 1, size=3))
+        bounds = [0, *cuts.tolist(), n]
+        parts = [oracle.attention_range(q, k, v, 0.4, causal, pads, lo, hi)
+                 for lo, hi in zip(bounds[:-1], bounds[1:])]
+        o, lse = oracle.merge_lse(parts)
+        ref = oracle.attention(q, k, v, 0.4, causal, pads)
+        _, lse_full = oracle.attention_range(q, k, v, 0.4, causal, pads)
+        if not np.array_equal(np.isinf(lse), np.isinf(lse_full)):
+            return False
+        fin = np.isfinite(lse_full)
+        worst = max(worst, np.abs(o - ref).max(), np.abs(lse[fin] - lse_full[fin]).max())
+    return worst <= TIGHT
+
+
+def pin_range_matches_recurrence():
+    """The (o, lse) of a range equals the recurrence's state over the same
+    range: o = acc / l and lse = m + log l."""
+    rng = np.random.default_rng(23)
+    worst = 0.0
+    for causal, pad, lo, hi in [(False, 0, 5, 27), (True, 0, 4, 30), (True, 6, 0, 17)]:
+        n = m = 30
+        q, k, v = rnd(rng, n, 8, scale=3.0), rnd(rng, m, 8, scale=3.0), rnd(rng, m, 5)
+        o, lse = oracle.attention_range(q[None, None], k[None, None], v[None, None], 0.5,
+                                        causal, None if pad == 0 else [pad], lo, hi)
+        mm, ll, acc = oracle.online_partial(q, np.arange(n), k, v, 0.5, 7, lo, hi, causal, pad)
+        fin = ll > 0
+        if not np.array_equal(fin, np.isfinite(lse[0, 0])):
+            return False
+        worst = max(worst, np.abs(o[0, 0] - oracle.finish(mm, ll, acc)).max(),
+                    np.abs(lse[0, 0][fin] - (mm[fin] + np.log(ll[fin]))).max(initial=0.0))
+    return worst <= TIGHT
+
+
 PINS = [pin_bruteforce_prefill, pin_bruteforce_gqa, pin_bruteforce_paged, pin_causal_row0,
         pin_causal_prefix_means, pin_hot_finite, pin_dominant_key, pin_recurrence_sweep,
         pin_split_merge,
-        pin_gqa_equals_repeated_mha, pin_paged_equals_contiguous]
+        pin_gqa_equals_repeated_mha, pin_paged_equals_contiguous,
+        pin_range_bruteforce, pin_range_merge, pin_range_matches_recurrence]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -599,7 +682,41 @@ def _online_partial_no_alpha(q_rows, row_idx, k, v, scale, tile, key_lo=0, key_h
     return m_run, l_run, acc
 
 
+def _range_ignores_begin(q, k, v, scale, causal=False, pads=None, key_begin=0, key_end=None):
+    return oa_attention_range(q, k, v, scale, causal, pads, 0, key_end)
+
+
+def _range_lse_without_max(q, k, v, scale, causal=False, pads=None, key_begin=0, key_end=None):
+    o, lse = oa_attention_range(q, k, v, scale, causal, pads, key_begin, key_end)
+    # forgets to add the max back: log(sum exp(s - max)) only
+    B, Hq, n, _ = q.shape
+    group = Hq // k.shape[1]
+    ke = k.shape[2] if key_end is None else key_end
+    for b in range(B):
+        pad = 0 if pads is None else int(pads[b])
+        lo = max(key_begin, pad)
+        if lo >= ke:
+            continue
+        for h in range(Hq):
+            s = oa.scores(q[b, h], k[b, h // group, lo:ke], scale)
+            ok = oa.allowed_keys(np.arange(n), np.arange(lo, ke), causal, pad)
+            mx = np.where(ok, s, -np.inf).max(axis=1)
+            lse[b, h] = np.where(np.isfinite(mx), lse[b, h] - np.where(np.isfinite(mx), mx, 0), -np.inf)
+    return o, lse
+
+
+def _merge_lse_wrong_sign(parts):
+    flipped = [(o_s, np.where(np.isfinite(l_s), -l_s, l_s)) for o_s, l_s in parts]
+    return oa_merge_lse(flipped)
+
+
+oa_attention_range = oa.attention_range
+oa_merge_lse = oa.merge_lse
+
 MUTANTS = {
+    "range_ignores_key_begin": ("attention_range", _range_ignores_begin),
+    "range_lse_without_max": ("attention_range", _range_lse_without_max),
+    "merge_lse_wrong_sign": ("merge_lse", _merge_lse_wrong_sign),
     "scores_without_scale": ("scores", _scores_noscale),
     "scores_scaled_twice": ("scores", _scores_double_scale),
     "scores_wrong_sign": ("scores", _scores_sign),
