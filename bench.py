@@ -93,6 +93,50 @@ def cpu_baseline(w, x, budget_s: float):
                       f"float64, {t_used:.1f} s"}
 
 
+def time_key_split(fa, q, k, v, wp, iters: int):
+    """The same prefill as four 512-key pieces (fa_fwd_partial) merged by
+    fa_merge; timed outside the step, after it, with HIP events."""
+    import torch
+    if iters <= 0:
+        return None
+    bounds = [0, 512, 1024, 1536, 2048]
+    B, Hq, n, dv = q.shape
+    o_parts = torch.empty((4, B, Hq, n, dv), dtype=torch.float32, device=q.device)
+    l_parts = torch.empty((4, B, Hq, n), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record()
+        for i, (lo, hi) in enumerate(zip(bounds[:-1], bounds[1:])):
+            fa.fwd_partial(q, k, v, lo, hi, scale=wp.scale, out=o_parts[i], lse=l_parts[i])
+        if ev is not None:
+            ev[1].record()
+        fa.merge(o_parts, l_parts, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(max(10, iters // 2)):
+        run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    rows = B * Hq * n
+    merge_bytes = 4 * rows * (dv + 1) * 4 + rows * dv * 2
+    from tiled_online_softmax_04_amd import inputs as gen
+    flops = gen.prefill_flops(wp)
+    return {"workload": "the prefill above as keys [0,512) [512,1024) [1024,1536) [1536,2048) "
+                        "through fa_fwd_partial, then fa_merge",
+            "tflops_total": round(flops / ((part_ms + merge_ms) * 1e-3) / 1e12, 2),
+            "tflops_pieces": round(flops / (part_ms * 1e-3) / 1e12, 2),
+            "pieces_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5),
+            "merge_gbps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
+            "merge_bytes": merge_bytes, "iters": iters}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +146,8 @@ def main():
                          "reach steady clocks")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
+    ap.add_argument("--key-split-iters", type=int, default=30,
+                    help="timed runs of the key-split variant after the step (0 skips it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -177,6 +223,8 @@ def main():
     pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
     dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
 
+    key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
+
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
     dec_traffic = read_traffic("fa_decode_cfg4_traffic.txt", DECODE_SOURCES)
 
@@ -215,6 +263,7 @@ def main():
                                 "kernels": "fa_decode_split + fa_decode_merge",
                                 "avg_call_ms": round(float(dec_ms.mean()), 5)}},
         "cpu_baseline": baseline,
+        "key_split": key_split,
     }
     print(json.dumps(out), flush=True)
 

@@ -85,6 +85,55 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
                  float scale, int causal, const int32_t* seq_lens, void* stream);
 
 /*
+ * fa_fwd_partial -- fa_fwd restricted to the keys in [key_begin, key_end), with
+ * the piece's state exposed so that pieces over disjoint key ranges can be
+ * merged (fa_merge).  This is the split of the key loop over workers that the
+ * S12 chapter describes for long sequences ("除了快，它还解锁了什么": flash-
+ * decoding and ring attention hand each other exactly these partial states)
+ * and its exercise 1 merges; here the state (m, l, acc) is given as
+ *
+ *   o   [batch, heads_q, n, dv] float32 (written): the output normalised over
+ *       the row's allowed keys inside the range, acc / l;
+ *   lse [batch, heads_q, n]     float32 (written): ln(sum of exp(scale * q.k))
+ *       over those keys, i.e. m + ln l with m in natural-log units.
+ *
+ * A row with no allowed key inside the range (padding, a causal row whose keys
+ * all lie at or beyond key_end, an empty range) gets o = 0 and lse = -inf.
+ * q, k, v, dtype, scale, causal and seq_lens mean what they mean in fa_fwd
+ * (masking and padding apply on top of the range); o must be 16-byte aligned
+ * and lse 4-byte aligned.  FA_ERR_INVALID additionally for a range outside
+ * 0 <= key_begin <= key_end <= m or a null lse (for non-empty work).
+ */
+fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* v, float* o,
+                         float* lse, int batch, int heads_q, int heads_kv, int n, int m, int d,
+                         int dv, float scale, int causal, const int32_t* seq_lens,
+                         int key_begin, int key_end, void* stream);
+
+/*
+ * fa_merge -- combine attention pieces over disjoint key ranges (the S12
+ * exercise 1 rescale applied to whole pieces): with L = max_s lse_s and
+ * w_s = exp(lse_s - L),
+ *
+ *   O   = sum_s w_s o_s / sum_s w_s          (rounded to out_dtype, RNE)
+ *   lse = L + ln(sum_s w_s)                  (if lse_out is not NULL)
+ *
+ *   o_parts   [parts, rows, dv] float32, lse_parts [parts, rows] float32 (read):
+ *             piece s of every row, as written by fa_fwd_partial (rows =
+ *             batch * heads_q * n for those tensors);
+ *   o         [rows, dv] of out_dtype (written); lse_out [rows] float32 or NULL.
+ *
+ * Pieces with lse_s = -inf are ignored (their o_s is not read); a row with no
+ * finite lse_s gets O = 0 and lse = -inf.  Merging the pieces of a partition
+ * of [0, m) reproduces fa_fwd up to rounding.  FA_ERR_INVALID: unknown dtype,
+ * parts <= 0, negative rows or dv, rows >= 2^31, null pointers (rows > 0),
+ * o_parts or o not 16-byte aligned, lse arrays not 4-byte aligned.
+ * FA_ERR_UNSUPPORTED: dv not a multiple of 4, or above 1024.  rows == 0
+ * returns FA_OK without launching.
+ */
+fa_status fa_merge(fa_dtype out_dtype, const float* o_parts, const float* lse_parts, int parts,
+                   long long rows, int dv, void* o, float* lse_out, void* stream);
+
+/*
  * fa_paged_decode_workspace_size -- bytes of device workspace fa_paged_decode needs
  * for these sizes (the split-K partial states).  Depends only on its arguments.
  * Returns 0 for arguments fa_paged_decode would reject.

@@ -32,8 +32,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_fwd", "fa_last_error", "fa_paged_decode",
-                                    "fa_paged_decode_workspace_size", "fa_status_string"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_partial", "fa_last_error", "fa_merge",
+                                    "fa_paged_decode", "fa_paged_decode_workspace_size",
+                                    "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -136,3 +137,55 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x)
+
+
+def partial(lib, dt=2, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, n=128, m=128, d=128, dv=128,
+            scale=0.088, causal=0, seq_lens=None, kb=0, ke=128):
+    return lib.fa_fwd_partial(dt, q, k, v, o, lse, B, Hq, Hkv, n, m, d, dv, scale, causal,
+                              seq_lens, kb, ke, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kb=-1), fa.FA_ERR_INVALID),
+    (dict(kb=10, ke=9), fa.FA_ERR_INVALID),
+    (dict(ke=129), fa.FA_ERR_INVALID),
+    (dict(lse=None), fa.FA_ERR_INVALID),
+    (dict(lse=ctypes.c_void_p(0x100002)), fa.FA_ERR_INVALID),
+    (dict(o=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(dt=5), fa.FA_ERR_INVALID),
+    (dict(causal=1, m=64, ke=64), fa.FA_ERR_INVALID),
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_partial_rejects_before_launch(lib, kw, code):
+    assert partial(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_partial_empty_work_is_ok(lib):
+    assert partial(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == fa.FA_OK
+
+
+def merge(lib, dt=2, op=P, lp=P, parts=2, rows=64, dv=128, o=P, lse_out=None):
+    return lib.fa_merge(dt, op, lp, parts, rows, dv, o, lse_out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=3), fa.FA_ERR_INVALID),
+    (dict(parts=0), fa.FA_ERR_INVALID),
+    (dict(rows=-1), fa.FA_ERR_INVALID),
+    (dict(dv=0), fa.FA_ERR_INVALID),
+    (dict(dv=63), fa.FA_ERR_UNSUPPORTED),
+    (dict(dv=66), fa.FA_ERR_UNSUPPORTED),
+    (dict(dv=1028), fa.FA_ERR_UNSUPPORTED),
+    (dict(rows=1 << 31), fa.FA_ERR_INVALID),
+    (dict(op=None), fa.FA_ERR_INVALID),
+    (dict(o=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(lse_out=ctypes.c_void_p(0x100001)), fa.FA_ERR_INVALID),
+])
+def test_merge_rejects_before_launch(lib, kw, code):
+    assert merge(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_merge_empty_rows_is_ok(lib):
+    assert merge(lib, rows=0, op=None, lp=None, o=None) == fa.FA_OK

@@ -1,0 +1,175 @@
+"""GPU parity of the key-range path: ``fa_fwd_partial`` (attention over keys in
+[key_begin, key_end) with its log-sum-exp) and ``fa_merge`` (the rescale that
+joins pieces of disjoint key ranges), against the float64 oracle's
+``attention_range`` / ``merge_lse`` / ``attention`` on the same seeded inputs.
+
+Bars: the output of a piece and of a merge meets the fa_fwd bar for the input
+dtype (max abs <= 1e-2 and mean abs <= 1e-3 for 16-bit inputs, 1e-5 for
+float32).  lse has no bar of its own in the pages; it is ln of a sum of
+weights that the kernels round to the input type (relative error below 2^-8),
+plus fp32 score rounding, so 16-bit inputs get |lse error| <= 1e-2 and float32
+inputs 1e-5, each plus two float32 ulps of |lse| because lse is stored as
+float32 (hot rows reach |lse| of several hundred, where an ulp is 3e-5).
+Rows without keys must give o = 0 and lse = -inf exactly."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tiled_online_softmax_04_amd import fa
+from tiled_online_softmax_04_amd import inputs as gen
+
+from gpu_util import assert_parity, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+
+
+def dev_inputs(x, dtype):
+    import torch
+    q, k, v = to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype)
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).cuda()
+    return q, k, v, sl
+
+
+def check_lse(got, ref, dtype, label):
+    inf_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), inf_ref), f"{label}: -inf pattern differs"
+    fin = ~inf_ref
+    assert np.all(np.isfinite(got[fin])), f"{label}: non-finite lse"
+    err = np.abs(got[fin] - ref[fin])
+    bound = LSE_TOL[dtype] + 2.0 ** -22 * np.abs(ref[fin])
+    say(f"  {label}: lse max_abs={float(err.max(initial=0.0)):.3e} "
+        f"worst err/bound={float((err / bound).max(initial=0.0)):.3f}")
+    assert np.all(err <= bound), f"{label}: lse error above {LSE_TOL[dtype]} + 2 ulp(|lse|)"
+
+
+CASES = [
+    # name, dtype, B, Hq, Hkv, n, m, d, causal, hot, lens, ranges
+    ("bf16_noncausal", "bf16", 2, 4, 4, 300, 300, 128, False, 1.0, None,
+     [(0, 300), (37, 211), (150, 150), (0, 5), (299, 300)]),
+    ("bf16_causal", "bf16", 1, 3, 3, 333, 333, 128, True, 1.0, None,
+     [(0, 333), (64, 128), (100, 333), (0, 1)]),
+    ("f16_causal_hot", "f16", 1, 2, 2, 520, 520, 128, True, 10.0, None, [(0, 260), (260, 520)]),
+    ("bf16_causal_leftpad", "bf16", 4, 2, 2, 400, 400, 128, True, 1.0, [400, 1, 0, 137],
+     [(0, 200), (200, 400), (250, 399)]),
+    ("bf16_gqa_d64", "bf16", 1, 8, 2, 200, 200, 64, True, 1.0, None, [(13, 190)]),
+    ("f16_n_ne_m", "f16", 2, 2, 1, 100, 333, 128, False, 1.0, None, [(0, 100), (100, 333)]),
+    ("f32_causal_leftpad_hot", "f32", 2, 2, 2, 100, 100, 64, True, 10.0, [100, 33],
+     [(0, 50), (50, 100), (7, 93)]),
+    ("f32_gqa_d128", "f32", 1, 4, 2, 77, 77, 128, False, 1.0, None, [(10, 60)]),
+]
+
+
+def make(case):
+    name, dtype, B, Hq, Hkv, n, m, d, causal, hot, lens, ranges = case
+    x = gen.make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, d,
+                                seed=zlib.crc32(name.encode()) % 1000, hot=hot, lens=lens)
+    return x, float(np.float32(1 / np.sqrt(d)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_partial_pieces(case):
+    import torch
+    name, dtype, causal, ranges = case[0], case[1], case[8], case[11]
+    say(f"[key-range] {name}")
+    x, scale = make(case)
+    q, k, v, sl = dev_inputs(x, dtype)
+    qf, kf, vf = (gen.to_f64(x[t], dtype) for t in ("q", "k", "v"))
+    for lo, hi in ranges:
+        o, lse = fa.fwd_partial(q, k, v, lo, hi, scale=scale, causal=causal, seq_lens=sl)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.attention_range(qf, kf, vf, scale, causal, x["pads"], lo, hi)
+        got_o, got_l = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        assert_parity(got_o, ref_o, dtype, f"{name} [{lo},{hi}) o")
+        check_lse(got_l, ref_l, dtype, f"{name} [{lo},{hi})")
+        none = np.isneginf(ref_l)
+        assert np.all(got_o[none] == 0), "rows without keys must give o = 0"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_merge_reproduces_full_pass(case):
+    import torch
+    name, dtype, B, Hq, n, m, causal = case[0], case[1], case[2], case[3], case[5], case[6], case[8]
+    say(f"[key-range merge] {name}")
+    x, scale = make(case)
+    q, k, v, sl = dev_inputs(x, dtype)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    cuts = np.sort(rng.integers(0, m + 1, size=2))
+    bounds = [0, *cuts.tolist(), m]                 # three ranges, possibly empty ones
+    pieces = [fa.fwd_partial(q, k, v, lo, hi, scale=scale, causal=causal, seq_lens=sl)
+              for lo, hi in zip(bounds[:-1], bounds[1:])]
+    o_parts = torch.stack([p[0] for p in pieces])
+    l_parts = torch.stack([p[1] for p in pieces])
+    out, lse = fa.merge(o_parts, l_parts, out_dtype=q.dtype, want_lse=True)
+    full = fa.fwd(q, k, v, scale=scale, causal=causal, seq_lens=sl)
+    torch.cuda.synchronize()
+    qf, kf, vf = (gen.to_f64(x[t], dtype) for t in ("q", "k", "v"))
+    ref = oracle.attention(qf, kf, vf, scale, causal, pads=x["pads"])
+    _, ref_l = oracle.attention_range(qf, kf, vf, scale, causal, x["pads"])
+    got = to_f64(out, dtype)
+    assert_parity(got, ref, dtype, f"{name} bounds={bounds} merged")
+    assert_parity(got, to_f64(full, dtype), dtype, f"{name} merged vs single pass")
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_l, dtype, f"{name} merged")
+    if x["pads"] is not None:
+        for b, p in enumerate(x["pads"]):
+            assert np.all(got[b, :, :p] == 0)
+
+
+def test_merge_kernel_on_oracle_pieces():
+    """The merge alone: pieces computed by the oracle (float32), merged on the
+    GPU, against the oracle's merge_lse; includes rows covered by no piece."""
+    import torch
+    rng = np.random.default_rng(31)
+    B, Hq, n, m, d = 2, 3, 50, 64, 64
+    q, k, v = (rng.standard_normal(s) for s in [(B, Hq, n, d), (B, Hq, m, d), (B, Hq, m, d)])
+    pads = [0, 20]
+    bounds = [0, 17, 17, 40, 64]
+    parts = [oracle.attention_range(q, k, v, 0.125, True, pads, lo, hi)
+             for lo, hi in zip(bounds[:-1], bounds[1:])]
+    o32 = [p_[0].astype(np.float32) for p_ in parts]
+    l32 = [p_[1].astype(np.float32) for p_ in parts]
+    ref_o, ref_l = oracle.merge_lse([(a.astype(np.float64), b.astype(np.float64))
+                                     for a, b in zip(o32, l32)])
+    o_parts = torch.from_numpy(np.stack(o32)).cuda()
+    l_parts = torch.from_numpy(np.stack(l32)).cuda()
+    for dt, label in [(torch.float32, "f32")]:
+        out, lse = fa.merge(o_parts, l_parts, out_dtype=dt, want_lse=True)
+        torch.cuda.synchronize()
+        assert_parity(out.cpu().numpy().astype(np.float64), ref_o, label, "merge of oracle pieces")
+        check_lse(lse.cpu().numpy().astype(np.float64), ref_l, label, "merge of oracle pieces")
+    out16 = fa.merge(o_parts, l_parts, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(out16, "bf16"), ref_o, "bf16", "merge of oracle pieces, bf16 out")
+
+
+def test_full_size_key_split_sampled():
+    """The bf16 2048-key workload split into four 512-key ranges, merged, on
+    sampled rows against the oracle; and the merged result against fa_fwd."""
+    import torch
+    w = gen.WORKLOADS["cfg2"]
+    say("[key-range] cfg2 in four key ranges")
+    x = gen.make_prefill(w)
+    q, k, v, _ = dev_inputs(x, w.dtype)
+    bounds = [0, 512, 1024, 1536, 2048]
+    pieces = [fa.fwd_partial(q, k, v, lo, hi, scale=w.scale) for lo, hi in zip(bounds[:-1],
+                                                                               bounds[1:])]
+    out = fa.merge(torch.stack([p[0] for p in pieces]), torch.stack([p[1] for p in pieces]),
+                   out_dtype=q.dtype)
+    full = fa.fwd(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    diff = (out.float() - full.float()).abs()
+    say(f"  merged vs single pass: max={diff.max().item():.3e} mean={diff.mean().item():.3e}")
+    assert diff.max().item() <= 1e-2 and diff.mean().item() <= 1e-3
+    rng = np.random.default_rng(77)
+    samples = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.n - 1)] + \
+        [(int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.n))) for _ in range(30)]
+    got = np.stack([to_f64(out[b, h, i], w.dtype) for b, h, i in samples])
+    ref = np.stack([oracle.attend(gen.to_f64(x["q"][b, h, i], w.dtype)[None], [i],
+                                  gen.to_f64(x["k"][b, h], w.dtype),
+                                  gen.to_f64(x["v"][b, h], w.dtype), w.scale)[0]
+                    for b, h, i in samples])
+    assert_parity(got, ref, w.dtype, f"cfg2 key split ({len(samples)} sampled rows)")

@@ -46,10 +46,13 @@ const char* fa_status_string(fa_status s) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
-fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o, int batch,
-                 int heads_q, int heads_kv, int n, int m, int d, int dv, float scale, int causal,
-                 const int32_t* seq_lens, void* stream) {
-  g_last_error[0] = '\0';
+// Checks shared by fa_fwd and fa_fwd_partial.  Returns FA_OK with *empty set
+// when there is nothing to compute.
+static fa_status check_fwd(fa_dtype dt, const void* q, const void* k, const void* v,
+                           const void* o, int batch, int heads_q, int heads_kv, int n, int m,
+                           int d, int dv, float scale, int causal, const int32_t* seq_lens,
+                           bool* empty) {
+  *empty = false;
   if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
   if (batch < 0 || heads_q < 0 || heads_kv < 0 || n < 0 || m < 0 || d <= 0 || dv <= 0)
@@ -69,18 +72,74 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
     return fail(FA_ERR_INVALID, "one head holds 2^31 elements or more");
   if (!supported_head_dim(d) || dv != d)
     return fail(FA_ERR_UNSUPPORTED, "head dims d=%d dv=%d (need d == dv in {64, 128})", d, dv);
-  if (batch == 0 || heads_q == 0 || n == 0) return FA_OK;
-  if (!q || !o) return fail(FA_ERR_INVALID, "null q or o");
+  if (batch == 0 || heads_q == 0 || n == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (!q || !o) return fail(FA_ERR_INVALID, "null q or output");
   if (m > 0 && (!k || !v)) return fail(FA_ERR_INVALID, "null k or v");
   if (!aligned16(q) || !aligned16(o) || (m > 0 && (!aligned16(k) || !aligned16(v))))
     return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
   const long long grid = fa::fwd_grid_size((int)dt, batch, heads_q, n);
   if (grid >= (1LL << 31)) return fail(FA_ERR_INVALID, "grid too large (%lld)", grid);
+  return FA_OK;
+}
 
+fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o, int batch,
+                 int heads_q, int heads_kv, int n, int m, int d, int dv, float scale, int causal,
+                 const int32_t* seq_lens, void* stream) {
+  g_last_error[0] = '\0';
+  bool empty;
+  const fa_status s = check_fwd(dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
+                                causal, seq_lens, &empty);
+  if (s != FA_OK || empty) return s;
   fa::FwdArgs a{(int)dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, scale, causal ? 1 : 0,
-                seq_lens, stream};
+                seq_lens, stream, 0, m, 0, nullptr, nullptr};
   const hipError_t e = fa::launch_fwd(a);
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
+  return FA_OK;
+}
+
+fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* v, float* o,
+                         float* lse, int batch, int heads_q, int heads_kv, int n, int m, int d,
+                         int dv, float scale, int causal, const int32_t* seq_lens,
+                         int key_begin, int key_end, void* stream) {
+  g_last_error[0] = '\0';
+  bool empty;
+  const fa_status s = check_fwd(dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
+                                causal, seq_lens, &empty);
+  if (s != FA_OK) return s;
+  if (key_begin < 0 || key_end < key_begin || key_end > m)
+    return fail(FA_ERR_INVALID, "key range [%d, %d) outside [0, m = %d]", key_begin, key_end, m);
+  if (empty) return FA_OK;
+  if (!lse) return fail(FA_ERR_INVALID, "null lse");
+  if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID, "lse must be 4-byte aligned");
+  fa::FwdArgs a{(int)dt, q, k, v, nullptr, batch, heads_q, heads_kv, n, m, d, scale,
+                causal ? 1 : 0, seq_lens, stream, key_begin, key_end, 1, o, lse};
+  const hipError_t e = fa::launch_fwd(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd_partial launch");
+  return FA_OK;
+}
+
+fa_status fa_merge(fa_dtype out_dtype, const float* o_parts, const float* lse_parts, int parts,
+                   long long rows, int dv, void* o, float* lse_out, void* stream) {
+  g_last_error[0] = '\0';
+  if (out_dtype != FA_DTYPE_F32 && out_dtype != FA_DTYPE_F16 && out_dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", (int)out_dtype);
+  if (parts <= 0 || rows < 0 || dv <= 0)
+    return fail(FA_ERR_INVALID, "bad sizes (parts=%d rows=%lld dv=%d)", parts, rows, dv);
+  if (dv % 4 != 0 || dv > 1024)
+    return fail(FA_ERR_UNSUPPORTED, "dv must be a multiple of 4 up to 1024 (got %d)", dv);
+  if (rows >= (1LL << 31)) return fail(FA_ERR_INVALID, "rows at or above 2^31");
+  if (rows == 0) return FA_OK;
+  if (!o_parts || !lse_parts || !o) return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(o_parts) || !aligned16(o))
+    return fail(FA_ERR_INVALID, "o_parts and o must be 16-byte aligned");
+  if (((uintptr_t)lse_parts & 3u) != 0 || ((uintptr_t)lse_out & 3u) != 0)
+    return fail(FA_ERR_INVALID, "lse arrays must be 4-byte aligned");
+  fa::MergeArgs a{(int)out_dtype, o_parts, lse_parts, parts, rows, dv, o, lse_out, stream};
+  const hipError_t e = fa::launch_merge(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_merge launch");
   return FA_OK;
 }
 

@@ -19,6 +19,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 // log2(e): the kernels work with exp2 and fold log2(e) into the fp32 score scale.
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // Finite start for the running max (in scaled log2 units).  Masked scores are
 // -inf, so exp2(-inf - kSentinel) = 0 and a fully masked tile leaves the state
 // untouched instead of producing exp2(-inf - -inf) = NaN.

@@ -18,7 +18,30 @@ struct FwdArgs {
   int causal;
   const int32_t* seq_lens;
   void* stream;
+  // Key range [key_begin, key_end) (0 and m for a full call).  With partial,
+  // the result goes to o_f32 (float32, normalised over the range) and lse
+  // (natural log of the range's softmax denominator) instead of o.
+  int key_begin, key_end;
+  int partial;
+  float* o_f32;
+  float* lse;
 };
+
+// Merge of key-range pieces: o_parts [parts, rows, dv] and lse_parts
+// [parts, rows] (float32) into o [rows, dv] of out_dtype and, if non-null,
+// lse_out [rows].
+struct MergeArgs {
+  int out_dtype;
+  const float* o_parts;
+  const float* lse_parts;
+  int parts;
+  long long rows;
+  int dv;
+  void* o;
+  float* lse_out;
+  void* stream;
+};
+hipError_t launch_merge(const MergeArgs& a);
 
 struct DecodeArgs {
   int dtype;

@@ -143,14 +143,18 @@ __device__ __forceinline__ void bare_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <class T, int D, bool CAUSAL, bool RAGGED>
+// PARTIAL: attend only to keys in [key_begin, key_end) and write the result
+// normalised over that range as float32 (Of) together with the natural-log
+// softmax denominator of the range (Lse), instead of the final O.
+template <class T, int D, bool CAUSAL, bool RAGGED, bool PARTIAL>
 #ifndef FA_PREFILL_WAVES_PER_EU
 #define FA_PREFILL_WAVES_PER_EU (kWaves / 4)
 #endif
 __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, const int32_t* __restrict__ seq_lens,
-    int Hq, int group, int n, int m, int q_tiles, int total, float c) {
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Of,
+    float* __restrict__ Lse, const int32_t* __restrict__ seq_lens, int Hq, int group, int n,
+    int m, int key_begin, int key_end, int q_tiles, int total, float c) {
   using G = Geo<D>;
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -173,7 +177,6 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   const uint16_t* Qh = Q + q_base;
   const uint16_t* Kh = K + kv_base;
   const uint16_t* Vh = V + kv_base;
-  uint16_t* Oh = O + q_base;
 
   // Padding rows of a left-padded sequence; out-of-range lengths are clamped.
   const int pad =
@@ -190,17 +193,22 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     q_ok[nt] = qrow[nt] < n && qrow[nt] >= pad;
   }
 
+  // Keys this call may attend: [key_lo, key_hi) -- past the left pad and
+  // inside the requested range (the whole of [0, m) for a full call).
+  const int key_lo = max(RAGGED ? pad : 0, key_begin);
+  const int key_hi = min(m, key_end);
   // Key range of this workgroup, in whole tiles.
-  const int kv_begin = RAGGED ? (pad / kBc) * kBc : 0;
-  const int kv_end = CAUSAL ? min(m, wg_q1) : m;
+  const int kv_begin = (key_lo / kBc) * kBc;
+  const int kv_end = CAUSAL ? min(key_hi, wg_q1) : key_hi;
+  const bool no_keys = (RAGGED && wg_q1 <= pad) || kv_end <= key_lo;
   const int t_begin = kv_begin / kBc;
-  const int t_end = (RAGGED && wg_q1 <= pad) ? t_begin : (kv_end + kBc - 1) / kBc;
-  const int key_lo = RAGGED ? pad : 0;
+  const int t_end = no_keys ? t_begin : (kv_end + kBc - 1) / kBc;
 
-  // K and V of this head as buffers that start at the first valid key: rows
-  // before it (padding) and from m on read back as zeros, so no tile ever
-  // needs clamping and padding contents never reach the arithmetic.
-  const uint32_t kv_bytes = (uint32_t)(m - key_lo) * (uint32_t)(D * 2);
+  // K and V of this head as buffers over exactly [key_lo, key_hi): rows
+  // before it (padding, or keys below the range) and from key_hi on read
+  // back as zeros, so no tile ever needs clamping and padding contents never
+  // reach the arithmetic.
+  const uint32_t kv_bytes = (uint32_t)max(key_hi - key_lo, 0) * (uint32_t)(D * 2);
   const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(Kh + (size_t)key_lo * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(Vh + (size_t)key_lo * D, kv_bytes);
 
@@ -332,8 +340,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
       // Mask only tiles that straddle the diagonal, the pad or the end of K
       // (a real branch: most tiles need no mask at all).
-      const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0) || (j0 + kBc > m) ||
-                             (RAGGED && j0 < pad);
+      const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0) || (j0 + kBc > key_hi) ||
+                             (j0 < key_lo);
       if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
             const int key = j0 + 32 * mt + kk;
-            const bool kbad = key >= m || (RAGGED && key < pad);
+            const bool kbad = key >= key_hi || key < key_lo;
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
               const bool bad = kbad || (CAUSAL && key > qrow[nt]);
@@ -420,12 +428,41 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   }
 
   // -------- epilogue: O = acc / l, zero for rows without keys --------
+  if constexpr (PARTIAL) {
+    // float32 O of the range and lse = ln(2^m * l) (m is in log2 units).
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const float l_tot = sum_xor32(l_run[nt]);
+      const bool has = l_tot > 0.f && q_ok[nt];
+      const float inv = has ? 1.f / l_tot : 0.f;
+      if (qrow[nt] < n) {
+        float* orow = Of + q_base + (size_t)qrow[nt] * D;
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int dv0 = 32 * t2 + 8 * g + 4 * hf;
+            float4 x;
+            x.x = acc[t2][nt][4 * g] * inv;
+            x.y = acc[t2][nt][4 * g + 1] * inv;
+            x.z = acc[t2][nt][4 * g + 2] * inv;
+            x.w = acc[t2][nt][4 * g + 3] * inv;
+            *reinterpret_cast<float4*>(orow + dv0) = x;
+          }
+        }
+        if (hf == 0)
+          Lse[q_base / D + qrow[nt]] =
+              has ? (m_run[nt] + log2f(l_tot)) * kLn2 : -__builtin_inff();
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const float l_tot = sum_xor32(l_run[nt]);
     const float inv = (l_tot > 0.f && q_ok[nt]) ? 1.f / l_tot : 0.f;
     if (qrow[nt] < n) {
-      uint16_t* orow = Oh + (size_t)qrow[nt] * D;
+      uint16_t* orow = O + q_base + (size_t)qrow[nt] * D;
 #pragma unroll
       for (int t2 = 0; t2 < G::kOTiles; ++t2) {
 #pragma unroll
@@ -449,11 +486,13 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 constexpr int kF32Rows = 16;
 constexpr int kF32Tile = 16;
 
-template <int D, bool CAUSAL, bool RAGGED>
+// PARTIAL: keys restricted to [key_begin, key_end); also writes the natural
+// log of the range's softmax denominator (Lse).  O is float32 either way.
+template <int D, bool CAUSAL, bool RAGGED, bool PARTIAL>
 __global__ __launch_bounds__(256) void fa_fwd_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, const int32_t* __restrict__ seq_lens, int Hq, int group, int n, int m,
-    int q_tiles, double scale) {
+    float* __restrict__ O, float* __restrict__ Lse, const int32_t* __restrict__ seq_lens, int Hq,
+    int group, int n, int m, int key_begin, int key_end, int q_tiles, double scale) {
   constexpr int S = D + 1;  // padded row stride (floats) against bank conflicts
   constexpr int E = D / 16; // output columns per lane
   __shared__ float q_s[kF32Rows * S];
@@ -483,10 +522,13 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
     q_s[r * S + d] = (row < n && row >= pad) ? Qh[(size_t)row * D + d] : 0.f;
   }
 
-  const int kv_begin = RAGGED ? (pad / kF32Tile) * kF32Tile : 0;
-  const int kv_end = CAUSAL ? min(m, q1) : m;
+  const int key_lo = max(RAGGED ? pad : 0, key_begin);
+  const int key_hi = min(m, key_end);
+  const int kv_begin = (key_lo / kF32Tile) * kF32Tile;
+  const int kv_end = CAUSAL ? min(key_hi, q1) : key_hi;
+  const bool no_keys = (RAGGED && q1 <= pad) || kv_end <= key_lo;
   const int t_begin = kv_begin / kF32Tile;
-  const int t_end = (RAGGED && q1 <= pad) ? t_begin : (kv_end + kF32Tile - 1) / kF32Tile;
+  const int t_end = no_keys ? t_begin : (kv_end + kF32Tile - 1) / kF32Tile;
 
   double m_run = -1.0e300, l_run = 0.0;
   double acc[E];
@@ -499,14 +541,14 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
     for (int x = tid; x < kF32Tile * D; x += 256) {
       const int r = x / D, d = x % D;
       const int key = j0 + r;
-      const bool ok = key < m && key >= pad;
+      const bool ok = key < key_hi && key >= key_lo;
       k_s[r * S + d] = ok ? Kh[(size_t)key * D + d] : 0.f;
       v_s[r * D + d] = ok ? Vh[(size_t)key * D + d] : 0.f;
     }
     __syncthreads();
 
     const int key = j0 + sub;
-    const bool ok = key < m && key >= pad && (!CAUSAL || key <= qrow) && q_ok;
+    const bool ok = key < key_hi && key >= key_lo && (!CAUSAL || key <= qrow) && q_ok;
     double s = 0.0;
 #pragma unroll 8
     for (int d = 0; d < D; ++d) s = fma((double)q_s[qi * S + d], (double)k_s[sub * S + d], s);
@@ -536,53 +578,67 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
     float* orow = Oh + (size_t)qrow * D + sub * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) orow[e] = (q_ok && l_tot > 0.0) ? (float)(acc[e] / l_tot) : 0.f;
+    if (PARTIAL && sub == 0)
+      Lse[((size_t)b * Hq + h) * n + qrow] =
+          (q_ok && l_tot > 0.0) ? (float)(m_run + log(l_tot)) : -__builtin_inff();
   }
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <class T, int D, bool C, bool R>
+template <class T, int D, bool C, bool R, bool P>
 static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
   const int q_tiles = (a.n + kBr - 1) / kBr;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
   const size_t lds = kStages * G::kStageElems * sizeof(uint16_t);
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R>),
+      reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R, P>),
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R>), dim3((unsigned)total), dim3(kThreads), lds,
+  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P>), dim3((unsigned)total), dim3(kThreads), lds,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (uint16_t*)a.o, a.seq_lens, a.heads_q,
-                     a.heads_q / a.heads_kv, a.n, a.m, q_tiles, (int)total,
-                     a.scale * kLog2e);
+                     (const uint16_t*)a.v, (uint16_t*)a.o, a.o_f32, a.lse, a.seq_lens,
+                     a.heads_q, a.heads_q / a.heads_kv, a.n, a.m, a.key_begin, a.key_end,
+                     q_tiles, (int)total, a.scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D, bool C, bool R>
+template <int D, bool C, bool R, bool P>
 static hipError_t launch_f32(const FwdArgs& a) {
   const int q_tiles = (a.n + kF32Rows - 1) / kF32Rows;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
-  hipLaunchKernelGGL((fa_fwd_f32<D, C, R>), dim3((unsigned)total), dim3(256), 0,
+  hipLaunchKernelGGL((fa_fwd_f32<D, C, R, P>), dim3((unsigned)total), dim3(256), 0,
                      (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k,
-                     (const float*)a.v, (float*)a.o, a.seq_lens, a.heads_q,
-                     a.heads_q / a.heads_kv, a.n, a.m, q_tiles, (double)a.scale);
+                     (const float*)a.v, P ? a.o_f32 : (float*)a.o, a.lse, a.seq_lens, a.heads_q,
+                     a.heads_q / a.heads_kv, a.n, a.m, a.key_begin, a.key_end, q_tiles,
+                     (double)a.scale);
   return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T, int D, bool P>
 static hipError_t dispatch_mask(const FwdArgs& a) {
   const bool r = a.seq_lens != nullptr;
-  if (a.causal) return r ? launch_mfma<T, D, true, true>(a) : launch_mfma<T, D, true, false>(a);
-  return r ? launch_mfma<T, D, false, true>(a) : launch_mfma<T, D, false, false>(a);
+  if (a.causal)
+    return r ? launch_mfma<T, D, true, true, P>(a) : launch_mfma<T, D, true, false, P>(a);
+  return r ? launch_mfma<T, D, false, true, P>(a) : launch_mfma<T, D, false, false, P>(a);
 }
 
-template <int D>
+template <int D, bool P>
 static hipError_t dispatch_f32(const FwdArgs& a) {
   const bool r = a.seq_lens != nullptr;
-  if (a.causal) return r ? launch_f32<D, true, true>(a) : launch_f32<D, true, false>(a);
-  return r ? launch_f32<D, false, true>(a) : launch_f32<D, false, false>(a);
+  if (a.causal) return r ? launch_f32<D, true, true, P>(a) : launch_f32<D, true, false, P>(a);
+  return r ? launch_f32<D, false, true, P>(a) : launch_f32<D, false, false, P>(a);
+}
+
+template <bool P>
+static hipError_t dispatch_dtype(const FwdArgs& a) {
+  if (a.dtype == 2)
+    return a.d == 128 ? dispatch_mask<BF16, 128, P>(a) : dispatch_mask<BF16, 64, P>(a);
+  if (a.dtype == 1)
+    return a.d == 128 ? dispatch_mask<F16, 128, P>(a) : dispatch_mask<F16, 64, P>(a);
+  return a.d == 128 ? dispatch_f32<128, P>(a) : dispatch_f32<64, P>(a);
 }
 
 long long fwd_grid_size(int dtype, int batch, int heads_q, int n) {
@@ -591,9 +647,7 @@ long long fwd_grid_size(int dtype, int batch, int heads_q, int n) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.dtype == 2) return a.d == 128 ? dispatch_mask<BF16, 128>(a) : dispatch_mask<BF16, 64>(a);
-  if (a.dtype == 1) return a.d == 128 ? dispatch_mask<F16, 128>(a) : dispatch_mask<F16, 64>(a);
-  return a.d == 128 ? dispatch_f32<128>(a) : dispatch_f32<64>(a);
+  return a.partial ? dispatch_dtype<true>(a) : dispatch_dtype<false>(a);
 }
 
 }  // namespace fa

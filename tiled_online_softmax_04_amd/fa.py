@@ -39,6 +39,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                            _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                            ctypes.c_float, _c_int, _c_void_p, _c_void_p]
+    lib.fa_fwd_partial.restype = _c_int
+    lib.fa_fwd_partial.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   ctypes.c_float, _c_int, _c_void_p, _c_int, _c_int, _c_void_p]
+    lib.fa_merge.restype = _c_int
+    lib.fa_merge.argtypes = [_c_int, _c_void_p, _c_void_p, _c_int, ctypes.c_longlong, _c_int,
+                             _c_void_p, _c_void_p, _c_void_p]
     lib.fa_paged_decode_workspace_size.restype = ctypes.c_size_t
     lib.fa_paged_decode_workspace_size.argtypes = [_c_int] * 6
     lib.fa_paged_decode.restype = _c_int
@@ -132,6 +139,86 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, seq_lens=None
     check(lib.fa_fwd(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Hq, Hkv, n, m, d, dv,
                      float(scale), 1 if causal else 0, _ptr(seq_lens), _stream(stream)))
     return out
+
+
+def _check_qkv(q, k, v, seq_lens):
+    import torch
+    _require(q, "q", 4, q.device)
+    _require(k, "k", 4, q.device)
+    _require(v, "v", 4, q.device)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, n, d = q.shape
+    Bk, Hkv, m, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape[:3]) != (B, Hkv, m):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if seq_lens is not None:
+        _require(seq_lens, "seq_lens", 1, q.device)
+        if seq_lens.dtype != torch.int32 or seq_lens.shape[0] != B:
+            raise ValueError("seq_lens must be int32 [B]")
+    return B, Hq, Hkv, n, m, d, v.shape[3]
+
+
+def fwd_partial(q, k, v, key_begin: int, key_end: int, scale: float | None = None,
+                causal: bool = False, seq_lens=None, out=None, lse=None, stream=None):
+    """Attention over the keys in [key_begin, key_end) only.  Returns
+    (o float32 [B, Hq, n, dv], lse float32 [B, Hq, n]): o is normalised over
+    the row's allowed keys in the range, lse = ln(sum exp(scale * q.k)) over
+    them (-inf, with o = 0, where there are none).  Pieces of disjoint ranges
+    combine with ``merge``."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, n, m, d, dv = _check_qkv(q, k, v, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, n, dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    _require(out, "out", 4, q.device)
+    _require(lse, "lse", 3, q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Hq, n, dv):
+        raise ValueError("out must be float32 [B, Hq, n, dv]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, n):
+        raise ValueError("lse must be float32 [B, Hq, n]")
+    check(lib.fa_fwd_partial(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                             B, Hq, Hkv, n, m, d, dv, float(scale), 1 if causal else 0,
+                             _ptr(seq_lens), int(key_begin), int(key_end), _stream(stream)))
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None, want_lse: bool = False,
+          stream=None):
+    """Combine pieces over disjoint key ranges: o_parts float32 [P, ..., dv]
+    and lse_parts float32 [P, ...] (stacked ``fwd_partial`` results) give
+    O [..., dv] in out_dtype (default bfloat16) and, with want_lse or lse_out,
+    the merged lse [...]."""
+    import torch
+    lib = load_library()
+    dev = o_parts.device
+    if not o_parts.is_cuda or not lse_parts.is_cuda:
+        raise ValueError("o_parts and lse_parts must be device tensors")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be float32")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape) or o_parts.dim() < 2:
+        raise ValueError("o_parts must be lse_parts' shape plus a trailing dv")
+    P, dv = o_parts.shape[0], o_parts.shape[-1]
+    row_shape = tuple(o_parts.shape[1:-1])
+    rows = int(math.prod(row_shape))
+    if out is None:
+        out = torch.empty((*row_shape, dv), dtype=out_dtype or torch.bfloat16, device=dev)
+    if (want_lse or lse_out is not None) and lse_out is None:
+        lse_out = torch.empty(row_shape, dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (*row_shape, dv) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out has the wrong shape or layout")
+    if lse_out is not None and (tuple(lse_out.shape) != row_shape or lse_out.dtype != torch.float32
+                                or not lse_out.is_contiguous() or not lse_out.is_cuda):
+        raise ValueError("lse_out must be float32 with the rows' shape")
+    check(lib.fa_merge(_dtype_code(out), _ptr(o_parts), _ptr(lse_parts), P, rows, dv, _ptr(out),
+                       _ptr(lse_out), _stream(stream)))
+    return (out, lse_out) if lse_out is not None else out
 
 
 def paged_decode_workspace_size(num_seqs, heads_q, heads_kv, dv, max_blocks_per_seq,
