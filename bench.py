@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -137,6 +138,41 @@ def time_key_split(fa, q, k, v, wp, iters: int):
             "merge_bytes": merge_bytes, "iters": iters}
 
 
+def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
+    """Peak device memory of one attention head, beyond its inputs and output:
+    the tiled library call against the plain three-step evaluation that keeps
+    S and P (float32) in device memory (exercise 3 of the S12 chapter)."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    for n in sizes:
+        g = torch.Generator(device="cpu").manual_seed(n)
+        q, k, v = (torch.randn((1, 1, n, d), generator=g).to(torch.bfloat16).to(dev)
+                   for _ in range(3))
+        o = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(d)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
+        fa.fwd(q, k, v, scale=scale, out=o)
+        torch.cuda.synchronize()
+        flash_extra = torch.cuda.max_memory_allocated(dev) - base
+        torch.cuda.reset_peak_memory_stats(dev)
+        kt = k.float()[0, 0].t().contiguous()
+        base2 = torch.cuda.memory_allocated(dev)
+        s = (q.float()[0, 0] @ kt) * scale          # S [n, n] float32
+        p_ = torch.softmax(s, dim=-1)               # P [n, n] float32
+        o2 = (p_ @ v.float()[0, 0]).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        naive_extra = torch.cuda.max_memory_allocated(dev) - base2
+        out.append({"n": n, "flash_extra_bytes": int(flash_extra),
+                    "naive_extra_bytes": int(naive_extra),
+                    "n2_float32_bytes": 4 * n * n})
+        del s, p_, o2, kt, q, k, v, o
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +184,9 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--key-split-iters", type=int, default=30,
                     help="timed runs of the key-split variant after the step (0 skips it)")
+    ap.add_argument("--peak-memory", type=int, default=1,
+                    help="1: also report peak device memory, tiled vs naive, at n = 512, 2048, "
+                         "8192 (0 skips it)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -224,6 +263,7 @@ def main():
     dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
 
     key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
+    mem = peak_memory(fa) if args.peak_memory else None
 
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
     dec_traffic = read_traffic("fa_decode_cfg4_traffic.txt", DECODE_SOURCES)
@@ -264,6 +304,7 @@ def main():
                                 "avg_call_ms": round(float(dec_ms.mean()), 5)}},
         "cpu_baseline": baseline,
         "key_split": key_split,
+        "peak_memory": mem,
     }
     print(json.dumps(out), flush=True)
 

@@ -6,14 +6,14 @@ Python binding.  See ``oracle/sdpa.py`` for what each function follows.
 """
 from .sdpa import (SENTINEL, allowed_keys, attend, attention, attention_range, attention_rows,
                    finish, gather_paged, masked_softmax, merge_lse, merge_partials,
-                   online_attention,
-                   online_attention_q_outer, online_partial, paged_decode, probabilities,
-                   scores, split_key_attention)
+                   online_attention, online_attention_q_outer, online_partial, paged_decode,
+                   paged_prefill, probabilities, scores, split_key_attention)
 
 __all__ = [
     "SENTINEL", "allowed_keys", "attend", "attention", "attention_range", "attention_rows",
     "finish", "gather_paged", "masked_softmax", "merge_lse", "merge_partials",
     "online_attention",
-    "online_attention_q_outer", "online_partial", "paged_decode", "probabilities", "scores",
+    "online_attention_q_outer", "online_partial", "paged_decode", "paged_prefill",
+    "probabilities", "scores",
     "split_key_attention",
 ]

@@ -19,6 +19,8 @@ What it computes (all arithmetic in float64 on exactly upcast inputs):
   as S12 recommends against exp(-inf - -inf).
 * ``merge_partials`` / ``split_key_attention`` -- combining (m, l, o) states
   of disjoint key ranges (S12 flash-decoding and exercise 1).
+* ``paged_prefill`` -- a chunk of query tokens at the end of each sequence
+  over the same paged cache (bottom-right aligned causal mask).
 * ``attention_range`` / ``merge_lse`` -- the definition restricted to a key
   range, reported as the range's normalised output and the natural log of its
   softmax denominator (log-sum-exp), and the merge of such pieces.  This is
@@ -172,6 +174,37 @@ def paged_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_
             vg = gather_paged(v_cache, block_table[s], L, block_size, g)
             heads = slice(g * group, (g + 1) * group)
             out[s, heads] = attend(q[s, heads], np.full(group, L - 1), kg, vg, scale)
+    return out
+
+
+def paged_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table,
+                  seq_lens, block_size: int, scale: float, causal: bool = True) -> np.ndarray:
+    """A chunk of n query tokens per sequence over a paged, grouped-query KV
+    cache that already holds the chunk's own keys: q [S, Hq, n, d] ->
+    O [S, Hq, n, dv].  Query row i of sequence s is token L_s - n + i, so the
+    chunk is the last n tokens of the sequence; with ``causal`` it attends
+    keys 0 .. L_s - n + i, else all L_s keys.  Rows at negative positions
+    (n > L_s) have no keys and give 0.  The keys are the block-table walk of
+    S12 "实现" (the chapter notes each tile can come through the block table);
+    n = 1 is ``paged_decode``."""
+    S, Hq, n, _ = q.shape
+    Hkv = k_cache.shape[2]
+    group = Hq // Hkv
+    out = np.zeros((S, Hq, n, v_cache.shape[-1]), dtype=np.float64)
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L <= 0:
+            continue
+        pos = np.arange(L - n, L, dtype=np.int64)
+        live = pos >= 0
+        for g in range(Hkv):
+            kg = gather_paged(k_cache, block_table[s], L, block_size, g)
+            vg = gather_paged(v_cache, block_table[s], L, block_size, g)
+            for h in range(g * group, (g + 1) * group):
+                if causal:
+                    out[s, h, live] = attend(q[s, h, live], pos[live], kg, vg, scale, True)
+                else:
+                    out[s, h, live] = attend(q[s, h, live], pos[live], kg, vg, scale, False)
     return out
 
 

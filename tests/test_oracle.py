@@ -307,11 +307,78 @@ def pin_range_matches_recurrence():
     return worst <= TIGHT
 
 
+# --------------------------------------------------------------------------
+# paged chunked prefill: a chunk of queries at the end of each sequence
+# --------------------------------------------------------------------------
+def brute_force_paged_prefill(q, k_cache, v_cache, table, seq_lens, bs, scale, causal):
+    """Literal loops: gather each sequence's rows through the table one token
+    at a time; query row i is token L - n + i."""
+    S, Hq, n, _ = q.shape
+    Hkv = k_cache.shape[2]
+    out = np.zeros((S, Hq, n, v_cache.shape[-1]))
+    for s in range(S):
+        L = int(seq_lens[s])
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            ks = [k_cache[table[s, t // bs], t % bs, g] for t in range(L)]
+            vs = [v_cache[table[s, t // bs], t % bs, g] for t in range(L)]
+            for i in range(n):
+                pos = L - n + i
+                keys = [j for j in range(L) if (not causal or j <= pos)] if pos >= 0 else []
+                if not keys:
+                    continue
+                sc = [sum(float(q[s, h, i, c]) * float(ks[j][c]) for c in range(q.shape[3])) * scale
+                      for j in keys]
+                w = [math.exp(x) for x in sc]
+                tot = sum(w)
+                for wj, j in zip(w, keys):
+                    out[s, h, i] += wj / tot * vs[j]
+    return out
+
+
+def make_paged_chunk(rng, n, lens, S=3, Hq=4, Hkv=2, d=5, dv=6, bs=4, maxb=5):
+    q1, kc, vc, table, lens, bs = make_paged(rng, S=S, Hq=Hq, Hkv=Hkv, d=d, dv=dv, bs=bs,
+                                             lens=lens, maxb=maxb)
+    q = rnd(rng, S, Hq, n, d)
+    return q, kc, vc, table, lens, bs
+
+
+def pin_paged_prefill_bruteforce():
+    rng = np.random.default_rng(24)
+    worst = 0.0
+    for causal in (True, False):
+        q, kc, vc, table, lens, bs = make_paged_chunk(rng, 5, (0, 3, 12))   # n > L for seq 1
+        got = oracle.paged_prefill(q, kc, vc, table, lens, bs, 0.45, causal)
+        ref = brute_force_paged_prefill(q, kc, vc, table, lens, bs, 0.45, causal)
+        worst = max(worst, np.abs(got - ref).max())
+    return worst <= TIGHT
+
+
+def pin_paged_prefill_special_cases():
+    """n = 1 is the paged decode; a chunk covering whole equal-length
+    sequences is causal attention on the gathered rows."""
+    rng = np.random.default_rng(25)
+    q, kc, vc, table, lens, bs = make_paged_chunk(rng, 1, (1, 9, 16))
+    got = oracle.paged_prefill(q, kc, vc, table, lens, bs, 0.3, True)[:, :, 0]
+    dec = oracle.paged_decode(q[:, :, 0], kc, vc, table, lens, bs, 0.3)
+    worst = np.abs(got - dec).max()
+    L = 12
+    q, kc, vc, table, lens, bs = make_paged_chunk(rng, L, (L, L), S=2)
+    got = oracle.paged_prefill(q, kc, vc, table, lens, bs, 0.3, True)
+    for s in range(2):
+        kk = np.stack([kc[table[s, t // bs], t % bs] for t in range(L)], axis=1)  # [Hkv, L, d]
+        vv = np.stack([vc[table[s, t // bs], t % bs] for t in range(L)], axis=1)
+        ref = oracle.attention(q[s][None], kk[None], vv[None], 0.3, causal=True)[0]
+        worst = max(worst, np.abs(got[s] - ref).max())
+    return worst <= TIGHT
+
+
 PINS = [pin_bruteforce_prefill, pin_bruteforce_gqa, pin_bruteforce_paged, pin_causal_row0,
         pin_causal_prefix_means, pin_hot_finite, pin_dominant_key, pin_recurrence_sweep,
         pin_split_merge,
         pin_gqa_equals_repeated_mha, pin_paged_equals_contiguous,
-        pin_range_bruteforce, pin_range_merge, pin_range_matches_recurrence]
+        pin_range_bruteforce, pin_range_merge, pin_range_matches_recurrence,
+        pin_paged_prefill_bruteforce, pin_paged_prefill_special_cases]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -710,10 +777,30 @@ def _merge_lse_wrong_sign(parts):
     return oa_merge_lse(flipped)
 
 
+def _paged_prefill_top_left(q, k_cache, v_cache, block_table, seq_lens, block_size, scale,
+                            causal=True):
+    """Chunk rows placed at positions 0 .. n-1 instead of the end."""
+    S, Hq, n, _ = q.shape
+    Hkv = k_cache.shape[2]
+    group = Hq // Hkv
+    out = np.zeros((S, Hq, n, v_cache.shape[-1]))
+    for s in range(S):
+        L = int(seq_lens[s])
+        if L <= 0:
+            continue
+        for g in range(Hkv):
+            kg = oa.gather_paged(k_cache, block_table[s], L, block_size, g)
+            vg = oa.gather_paged(v_cache, block_table[s], L, block_size, g)
+            for h in range(g * group, (g + 1) * group):
+                out[s, h] = oa.attend(q[s, h], np.arange(n), kg, vg, scale, causal)
+    return out
+
+
 oa_attention_range = oa.attention_range
 oa_merge_lse = oa.merge_lse
 
 MUTANTS = {
+    "paged_prefill_top_left": ("paged_prefill", _paged_prefill_top_left),
     "range_ignores_key_begin": ("attention_range", _range_ignores_begin),
     "range_lse_without_max": ("attention_range", _range_lse_without_max),
     "merge_lse_wrong_sign": ("merge_lse", _merge_lse_wrong_sign),
