@@ -138,6 +138,34 @@ def time_key_split(fa, q, k, v, wp, iters: int):
             "merge_bytes": merge_bytes, "iters": iters}
 
 
+def time_paged_prefill(fa, wd, kc, vc, bt, sl, seq_lens, iters: int, n: int = 512):
+    """A 512-token causal chunk per sequence over the decode workload's paged
+    cache (the chunk being the last 512 tokens of each sequence); HIP events
+    around fa_paged_prefill, after the step."""
+    import torch
+    from tiled_online_softmax_04_amd import inputs as gen
+    if iters <= 0:
+        return None
+    g = torch.Generator(device="cpu").manual_seed(wd.seed + 1)
+    q = torch.randn((wd.num_seqs, wd.Hq, n, wd.d), generator=g).to(torch.bfloat16).to(kc.device)
+    out = torch.empty((wd.num_seqs, wd.Hq, n, wd.dv), dtype=q.dtype, device=q.device)
+    for _ in range(max(10, iters // 2)):
+        fa.paged_prefill(q, kc, vc, bt, sl, wd.block_size, scale=wd.scale, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fa.paged_prefill(q, kc, vc, bt, sl, wd.block_size, scale=wd.scale, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = gen.paged_prefill_flops(seq_lens, n, wd.Hq, wd.d, wd.dv, causal=True)
+    return {"workload": f"paged prefill bf16: a {n}-token causal chunk at the end of each of the "
+                        "decode workload's 64 sequences (Hq=32, Hkv=8, d=128, 16-token blocks, "
+                        "random placement)",
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 5), "flop": flops,
+            "iters": iters}
+
+
 def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
     """Peak device memory of one attention head, beyond its inputs and output:
     the tiled library call against the plain three-step evaluation that keeps
@@ -157,18 +185,24 @@ def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
         fa.fwd(q, k, v, scale=scale, out=o)
         torch.cuda.synchronize()
         flash_extra = torch.cuda.max_memory_allocated(dev) - base
-        torch.cuda.reset_peak_memory_stats(dev)
         kt = k.float()[0, 0].t().contiguous()
+
+        def naive():
+            s = (q.float()[0, 0] @ kt) * scale      # S [n, n] float32
+            p_ = torch.softmax(s, dim=-1)           # P [n, n] float32
+            return (p_ @ v.float()[0, 0]).to(torch.bfloat16)
+
+        naive()  # first use sets up the matrix library's own workspace
+        torch.cuda.synchronize()
         base2 = torch.cuda.memory_allocated(dev)
-        s = (q.float()[0, 0] @ kt) * scale          # S [n, n] float32
-        p_ = torch.softmax(s, dim=-1)               # P [n, n] float32
-        o2 = (p_ @ v.float()[0, 0]).to(torch.bfloat16)
+        torch.cuda.reset_peak_memory_stats(dev)
+        o2 = naive()
         torch.cuda.synchronize()
         naive_extra = torch.cuda.max_memory_allocated(dev) - base2
         out.append({"n": n, "flash_extra_bytes": int(flash_extra),
                     "naive_extra_bytes": int(naive_extra),
                     "n2_float32_bytes": 4 * n * n})
-        del s, p_, o2, kt, q, k, v, o
+        del o2, kt, q, k, v, o
         torch.cuda.empty_cache()
     return out
 
@@ -183,7 +217,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--key-split-iters", type=int, default=30,
-                    help="timed runs of the key-split variant after the step (0 skips it)")
+                    help="timed runs of the key-split and paged-prefill variants after the step "
+                         "(0 skips them)")
     ap.add_argument("--peak-memory", type=int, default=1,
                     help="1: also report peak device memory, tiled vs naive, at n = 512, 2048, "
                          "8192 (0 skips it)")
@@ -263,6 +298,7 @@ def main():
     dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
 
     key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
+    paged = time_paged_prefill(fa, wd, kc, vc, bt, sl, xd["seq_lens"], args.key_split_iters)
     mem = peak_memory(fa) if args.peak_memory else None
 
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
@@ -304,6 +340,7 @@ def main():
                                 "avg_call_ms": round(float(dec_ms.mean()), 5)}},
         "cpu_baseline": baseline,
         "key_split": key_split,
+        "paged_prefill": paged,
         "peak_memory": mem,
     }
     print(json.dumps(out), flush=True)

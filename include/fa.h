@@ -134,6 +134,39 @@ fa_status fa_merge(fa_dtype out_dtype, const float* o_parts, const float* lse_pa
                    long long rows, int dv, void* o, float* lse_out, void* stream);
 
 /*
+ * fa_paged_prefill -- a chunk of n query tokens per sequence attending over a
+ * paged KV cache that already holds the chunk's own keys and values: the
+ * prefill counterpart of fa_paged_decode.  The S12 chapter's paged loop walks
+ * the block table key block by key block ("实现"), and the chapter notes that
+ * each tile of the tiled pass can be such a block; here the K/V tiles of the
+ * prefill kernel are gathered through the table.
+ *
+ *   q           [num_seqs, heads_q, n, d]: query row i of sequence b is its
+ *               token L_b - n + i, i.e. the chunk is the last n tokens;
+ *   k_cache     [num_blocks, block_size, heads_kv, d ], v_cache likewise with dv;
+ *   block_table [num_seqs, max_blocks_per_seq] int32; entries at or past
+ *               ceil(L_b / block_size) are never read; used entries must be in
+ *               [0, num_blocks);
+ *   seq_lens    [num_seqs] int32 total lengths 0 <= L_b <= max_blocks_per_seq *
+ *               block_size, chunk included;
+ *   o           [num_seqs, heads_q, n, dv] (written).
+ *
+ * causal: nonzero -> row i attends keys 0 .. L_b - n + i (the mask aligned to
+ * the end of the sequence); zero -> all L_b keys.  Rows with L_b - n + i < 0
+ * (a chunk longer than its sequence) have no keys and are written as 0.
+ * Query head h reads KV head h / (heads_q / heads_kv).  n = 1 with causal is
+ * the decode of fa_paged_decode.
+ * Limits of this build: f16 or bf16 (f32 -> FA_ERR_UNSUPPORTED), d == dv in
+ * {64, 128}, max_blocks_per_seq <= 16384 (else FA_ERR_UNSUPPORTED).
+ * FA_ERR_INVALID: as fa_paged_decode, plus a negative n.  No workspace.
+ */
+fa_status fa_paged_prefill(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                           int num_seqs, int heads_q, int heads_kv, int n, int d, int dv,
+                           int num_blocks, int max_blocks_per_seq, float scale, int causal,
+                           void* o, void* stream);
+
+/*
  * fa_paged_decode_workspace_size -- bytes of device workspace fa_paged_decode needs
  * for these sizes (the split-K partial states).  Depends only on its arguments.
  * Returns 0 for arguments fa_paged_decode would reject.

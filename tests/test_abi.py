@@ -34,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_fwd", "fa_fwd_partial", "fa_last_error", "fa_merge",
                                     "fa_paged_decode", "fa_paged_decode_workspace_size",
-                                    "fa_status_string"]
+                                    "fa_paged_prefill", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -189,3 +189,31 @@ def test_merge_rejects_before_launch(lib, kw, code):
 
 def test_merge_empty_rows_is_ok(lib):
     assert merge(lib, rows=0, op=None, lp=None, o=None) == fa.FA_OK
+
+
+def pprefill(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, n=33, d=128, dv=128,
+             NB=64, maxb=16, scale=0.088, causal=1, o=P):
+    return lib.fa_paged_prefill(dt, q, kc, vc, bt, sl, bs, S, Hq, Hkv, n, d, dv, NB, maxb, scale,
+                                causal, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), fa.FA_ERR_INVALID),
+    (dict(n=-1), fa.FA_ERR_INVALID),
+    (dict(bs=0), fa.FA_ERR_INVALID),
+    (dict(NB=0), fa.FA_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(bt=None), fa.FA_ERR_INVALID),
+    (dict(o=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(maxb=16385), fa.FA_ERR_UNSUPPORTED),
+])
+def test_paged_prefill_rejects_before_launch(lib, kw, code):
+    assert pprefill(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_paged_prefill_empty_chunk_is_ok(lib):
+    assert pprefill(lib, n=0, q=None, o=None) == fa.FA_OK

@@ -1,0 +1,104 @@
+"""GPU parity of the paged chunked prefill (fa_paged_prefill): a chunk of n
+query tokens at the end of each sequence over a block-table KV cache, against
+the float64 oracle's paged_prefill on the same seeded inputs (block tables are
+random permutations; cache tails and unused table entries are poisoned).  Bar:
+max abs <= 1e-2 and mean abs <= 1e-3 for bf16 / fp16, no inf/NaN, rows with no
+keys exactly 0."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+from tiled_online_softmax_04_amd import fa
+from tiled_online_softmax_04_amd import inputs as gen
+
+from gpu_util import assert_parity, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def run(x, dtype, bs, scale, causal):
+    import torch
+    q = to_dev(x["q"], dtype)
+    kc, vc = to_dev(x["k_cache"], dtype), to_dev(x["v_cache"], dtype)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seq_lens"]).cuda()
+    o = fa.paged_prefill(q, kc, vc, bt, sl, bs, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o
+
+
+def oracle_of(x, dtype, bs, scale, causal):
+    return oracle.paged_prefill(gen.to_f64(x["q"], dtype), gen.to_f64(x["k_cache"], dtype),
+                                gen.to_f64(x["v_cache"], dtype), x["block_table"], x["seq_lens"],
+                                bs, scale, causal)
+
+
+CASES = [
+    # name, dtype, S, Hq, Hkv, d, bs, lens, maxb, n, causal
+    ("bf16_bs16_causal", "bf16", 3, 8, 2, 128, 16, [300, 77, 700], 48, 77, True),
+    ("bf16_bs16_short_seq", "bf16", 2, 4, 4, 128, 16, [40, 400], 32, 100, True),   # n > L
+    ("f16_bs7_causal", "f16", 3, 4, 1, 128, 7, [130, 7, 301], 50, 64, True),
+    ("bf16_bs32_noncausal", "bf16", 2, 8, 8, 64, 32, [257, 64], 16, 90, False),
+    ("f16_d64_gqa_causal", "f16", 4, 16, 4, 64, 16, [1, 33, 129, 250], 20, 17, True),
+    ("bf16_whole_sequence", "bf16", 2, 2, 2, 128, 16, [256, 256], 16, 256, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_paged_prefill_small(case):
+    name, dtype, S, Hq, Hkv, d, bs, lens, maxb, n, causal = case
+    say(f"[paged prefill] {name}")
+    w = gen.Decode(name, dtype, S, Hq, Hkv, d, d, bs, 1, 1, maxb, seed=sum(map(ord, name)))
+    x = gen.make_paged_chunk(w, n, seq_lens=lens)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = to_f64(run(x, dtype, bs, scale, causal), dtype)
+    ref = oracle_of(x, dtype, bs, scale, causal)
+    assert_parity(got, ref, dtype, name)
+    for s, L in enumerate(lens):
+        if n > L:
+            assert np.all(got[s, :, :n - L] == 0), "rows before the sequence must be 0"
+
+
+def test_chunk_of_one_is_the_decode():
+    import torch
+    w = gen.WORKLOADS["cfg4"]
+    w = dataclasses.replace(w, num_seqs=8, len_lo=100, len_hi=3000, max_blocks_per_seq=200)
+    x = gen.make_paged_chunk(w, 1)
+    q = to_dev(x["q"], w.dtype)
+    kc, vc = to_dev(x["k_cache"], w.dtype), to_dev(x["v_cache"], w.dtype)
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seq_lens"]).cuda()
+    pre = fa.paged_prefill(q, kc, vc, bt, sl, w.block_size, scale=w.scale)[:, :, 0]
+    dec = fa.paged_decode(q[:, :, 0].contiguous(), kc, vc, bt, sl, w.block_size, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(pre, w.dtype), to_f64(dec, w.dtype), w.dtype, "n=1 prefill vs decode")
+
+
+def test_full_size_chunk_sampled():
+    """The decode workload's cache (64 sequences, lengths in [512, 8192], 16-token
+    blocks, random placement) with a 512-token chunk per sequence."""
+    import torch
+    w = gen.WORKLOADS["cfg4"]
+    n = 512
+    say("[paged prefill] cfg4 cache, 512-token chunks")
+    x = gen.make_paged_chunk(w, n)
+    o = run(x, w.dtype, w.block_size, w.scale, True)
+    assert bool(torch.isfinite(o.float()).all())
+    rng = np.random.default_rng(9)
+    samples = [(0, 0, 0), (w.num_seqs - 1, w.Hq - 1, n - 1)] + \
+        [(int(rng.integers(w.num_seqs)), int(rng.integers(w.Hq)), int(rng.integers(n)))
+         for _ in range(30)]
+    got = np.stack([to_f64(o[s, h, i], w.dtype) for s, h, i in samples])
+    ref = np.zeros_like(got)
+    for t, (s, h, i) in enumerate(samples):
+        L = int(x["seq_lens"][s])
+        g = h // (w.Hq // w.Hkv)
+        kk = gen.to_f64(oracle.gather_paged(x["k_cache"], x["block_table"][s], L, w.block_size, g),
+                        w.dtype)
+        vv = gen.to_f64(oracle.gather_paged(x["v_cache"], x["block_table"][s], L, w.block_size, g),
+                        w.dtype)
+        ref[t] = oracle.attend(gen.to_f64(x["q"][s, h, i], w.dtype)[None], [L - n + i], kk, vv,
+                               w.scale, True)[0]
+    assert_parity(got, ref, w.dtype, f"cfg4 cache chunk ({len(samples)} sampled rows)")

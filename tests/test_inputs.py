@@ -89,3 +89,24 @@ def test_small_workload_values(name):
         assert np.abs(s).max() > 200      # 'hot' scores of a few hundred
     else:
         assert np.abs(s).max() < 10
+
+
+def test_paged_chunk_shares_the_decode_cache():
+    w = gen.Decode("t", "bf16", 3, 4, 2, 64, 64, 16, 10, 90, 8, seed=11)
+    a = gen.make_paged_chunk(w, 5)
+    b = gen.make_paged_chunk(w, 5)
+    d = gen.make_decode(w)
+    assert a["q"].shape == (3, 4, 5, 64)
+    assert np.array_equal(a["q"], b["q"])
+    for k in ("k_cache", "v_cache", "block_table", "seq_lens"):
+        assert np.array_equal(a[k], d[k], equal_nan=True) if a[k].dtype.kind == "f" else \
+            np.array_equal(a[k], d[k])
+
+
+def test_paged_prefill_flops_closed_form():
+    # causal: row i of a chunk of n at the end of L tokens sees L - n + i + 1 keys
+    L, n = 100, 30
+    pairs = sum(L - n + i + 1 for i in range(n))
+    assert gen.paged_prefill_flops([L], n, 2, 64, 64) == pairs * 2 * (4 * 64)
+    assert gen.paged_prefill_flops([L], n, 1, 64, 64, causal=False) == n * L * 4 * 64
+    assert gen.paged_prefill_flops([3], 5, 1, 1, 1) == (1 + 2 + 3) * 4  # rows before 0 skipped

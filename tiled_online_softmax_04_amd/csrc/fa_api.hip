@@ -94,7 +94,7 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
                                 causal, seq_lens, &empty);
   if (s != FA_OK || empty) return s;
   fa::FwdArgs a{(int)dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, scale, causal ? 1 : 0,
-                seq_lens, stream, 0, m, 0, nullptr, nullptr};
+                seq_lens, stream, 0, m, 0, nullptr, nullptr, 0, nullptr, 0, 0, 0};
   const hipError_t e = fa::launch_fwd(a);
   if (e != hipSuccess) return hip_fail(e, "fa_fwd launch");
   return FA_OK;
@@ -115,9 +115,48 @@ fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* 
   if (!lse) return fail(FA_ERR_INVALID, "null lse");
   if (((uintptr_t)lse & 3u) != 0) return fail(FA_ERR_INVALID, "lse must be 4-byte aligned");
   fa::FwdArgs a{(int)dt, q, k, v, nullptr, batch, heads_q, heads_kv, n, m, d, scale,
-                causal ? 1 : 0, seq_lens, stream, key_begin, key_end, 1, o, lse};
+                causal ? 1 : 0, seq_lens, stream, key_begin, key_end, 1, o, lse, 0, nullptr, 0,
+                0, 0};
   const hipError_t e = fa::launch_fwd(a);
   if (e != hipSuccess) return hip_fail(e, "fa_fwd_partial launch");
+  return FA_OK;
+}
+
+static fa_status check_decode_sizes(int num_seqs, int heads_q, int heads_kv, int d, int dv,
+                                    int max_blocks_per_seq, int block_size);
+
+fa_status fa_paged_prefill(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                           int num_seqs, int heads_q, int heads_kv, int n, int d, int dv,
+                           int num_blocks, int max_blocks_per_seq, float scale, int causal,
+                           void* o, void* stream) {
+  g_last_error[0] = '\0';
+  if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
+  fa_status s = check_decode_sizes(num_seqs, heads_q, heads_kv, d, dv, max_blocks_per_seq,
+                                   block_size);
+  if (s != FA_OK) return s;
+  if (n < 0) return fail(FA_ERR_INVALID, "negative chunk length %d", n);
+  if (num_blocks <= 0) return fail(FA_ERR_INVALID, "num_blocks must be > 0");
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
+  if ((long long)n * d >= kMaxElems) return fail(FA_ERR_INVALID, "chunk too long");
+  if (dt == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "paged prefill supports f16 and bf16");
+  if (max_blocks_per_seq > fa::max_paged_blocks())
+    return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq above %d", fa::max_paged_blocks());
+  if (num_seqs == 0 || heads_q == 0 || n == 0) return FA_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+    return fail(FA_ERR_INVALID, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+  const long long grid = fa::fwd_grid_size((int)dt, num_seqs, heads_q, n);
+  if (grid >= (1LL << 31)) return fail(FA_ERR_INVALID, "grid too large (%lld)", grid);
+  fa::FwdArgs a{(int)dt, q, k_cache, v_cache, o, num_seqs, heads_q, heads_kv, n,
+                max_blocks_per_seq * block_size, d, scale, causal ? 1 : 0, seq_lens, stream, 0,
+                0, 0, nullptr, nullptr, 1, block_table, block_size, max_blocks_per_seq,
+                num_blocks};
+  const hipError_t e = fa::launch_fwd(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_paged_prefill launch");
   return FA_OK;
 }
 

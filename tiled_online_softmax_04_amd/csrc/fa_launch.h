@@ -25,6 +25,13 @@ struct FwdArgs {
   int partial;
   float* o_f32;
   float* lse;
+  // Paged chunk (f16 / bf16): k and v are caches [num_blocks, block_size,
+  // heads_kv, d] reached through block_table [batch, max_blocks]; seq_lens
+  // holds the total lengths; the n query rows are each sequence's last n
+  // tokens.
+  int paged;
+  const int32_t* block_table;
+  int block_size, max_blocks, num_blocks;
 };
 
 // Merge of key-range pieces: o_parts [parts, rows, dv] and lse_parts
@@ -59,6 +66,8 @@ struct DecodeArgs {
 
 // Number of workgroups fa_fwd launches (the host checks it fits a grid).
 long long fwd_grid_size(int dtype, int batch, int heads_q, int n);
+// Longest block table a paged prefill can stage (entries per sequence).
+int max_paged_blocks();
 hipError_t launch_fwd(const FwdArgs& a);
 
 // Split size (tokens) and split count of the paged decode, from sizes only.

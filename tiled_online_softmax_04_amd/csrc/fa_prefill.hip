@@ -108,6 +108,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
 }
 
+// The same from a 64-bit global address per lane (used where the rows of a
+// tile come from scattered cache blocks).
+__device__ __forceinline__ void gdma16(const void* src, lds_char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
 // Transposing LDS read: within each 16 lanes, lane 4r+t names row r, columns
 // 4t..4t+3; lane c receives column c of the 4 rows.  Issued from inline asm so
 // that the byte offset OFF lands in the instruction's offset field; the result
@@ -146,7 +152,10 @@ __device__ __forceinline__ void bare_barrier() {
 // PARTIAL: attend only to keys in [key_begin, key_end) and write the result
 // normalised over that range as float32 (Of) together with the natural-log
 // softmax denominator of the range (Lse), instead of the final O.
-template <class T, int D, bool CAUSAL, bool RAGGED, bool PARTIAL>
+// PAGED: K and V are paged caches [num_blocks, bs, Hkv, D] reached through
+// block_table; the n query rows of sequence b are its last n tokens (row i is
+// token seq_lens[b] - n + i) and the causal mask is aligned to that.
+template <class T, int D, bool CAUSAL, bool RAGGED, bool PARTIAL, bool PAGED>
 #ifndef FA_PREFILL_WAVES_PER_EU
 #define FA_PREFILL_WAVES_PER_EU (kWaves / 4)
 #endif
@@ -154,7 +163,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Of,
     float* __restrict__ Lse, const int32_t* __restrict__ seq_lens, int Hq, int group, int n,
-    int m, int key_begin, int key_end, int q_tiles, int total, float c) {
+    int m, int key_begin, int key_end, int q_tiles, int total, float c,
+    const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks) {
   using G = Geo<D>;
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   const int Hkv = Hq / group;
 
   const size_t q_base = ((size_t)b * Hq + h) * (size_t)n * D;
-  const size_t kv_base = ((size_t)b * Hkv + hkv) * (size_t)m * D;
+  const size_t kv_base = PAGED ? 0 : ((size_t)b * Hkv + hkv) * (size_t)m * D;
   const uint16_t* Qh = Q + q_base;
   const uint16_t* Kh = K + kv_base;
   const uint16_t* Vh = V + kv_base;
@@ -181,6 +191,9 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   // Padding rows of a left-padded sequence; out-of-range lengths are clamped.
   const int pad =
       RAGGED ? __builtin_amdgcn_readfirstlane(min(max(n - seq_lens[b], 0), n)) : 0;
+  // Paged chunk: key position of query row i is qoff + i, qoff = L - n.
+  const int L = PAGED ? __builtin_amdgcn_readfirstlane(min(max(seq_lens[b], 0), maxb * bs)) : 0;
+  const int qoff = PAGED ? L - n : 0;
   const int wg_q0 = qt * kBr;
   const int wg_q1 = min(n, wg_q0 + kBr);
   const int wq0 = wg_q0 + w * kQPerWave;  // first query of this wave
@@ -189,18 +202,20 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     qrow[nt] = wq0 + 32 * nt + ql;
-    // Rows that hold no real query: past n, or inside the left pad.
-    q_ok[nt] = qrow[nt] < n && qrow[nt] >= pad;
+    // Rows that hold no real query: past n, inside the left pad, or (paged)
+    // before the first token of the sequence.
+    q_ok[nt] = qrow[nt] < n && (PAGED ? qrow[nt] + qoff >= 0 : qrow[nt] >= pad);
   }
 
   // Keys this call may attend: [key_lo, key_hi) -- past the left pad and
   // inside the requested range (the whole of [0, m) for a full call).
-  const int key_lo = max(RAGGED ? pad : 0, key_begin);
-  const int key_hi = min(m, key_end);
+  const int key_lo = PAGED ? 0 : max(RAGGED ? pad : 0, key_begin);
+  const int key_hi = PAGED ? L : min(m, key_end);
   // Key range of this workgroup, in whole tiles.
   const int kv_begin = (key_lo / kBc) * kBc;
-  const int kv_end = CAUSAL ? min(key_hi, wg_q1) : key_hi;
-  const bool no_keys = (RAGGED && wg_q1 <= pad) || kv_end <= key_lo;
+  const int kv_end = CAUSAL ? min(key_hi, wg_q1 + qoff) : key_hi;
+  const bool no_keys = (RAGGED && wg_q1 <= pad) || (PAGED && wg_q1 + qoff <= 0) ||
+                       kv_end <= key_lo;
   const int t_begin = kv_begin / kBc;
   const int t_end = no_keys ? t_begin : (kv_end + kBc - 1) / kBc;
 
@@ -217,6 +232,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   // and logical chunk that belong there (kappa rows for K, swizzled chunks for
   // both).  The per-lane byte offsets within a tile never change.
   uint32_t dma_off[G::kDmaPerWave];
+  int dma_key[G::kDmaPerWave], dma_col[G::kDmaPerWave];  // paged: key in tile, first column
   const bool dma_v = w * G::kDmaPerWave >= G::kDmaPerTile;  // first half of the waves: K
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
@@ -226,18 +242,44 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     const int klocal = dma_v ? p : ((p & ~31) | kappa(p & 31));
     const int chunk = pc ^ (dma_v ? v_swz<D>(p) : k_swz<D>(p));
     dma_off[i] = (uint32_t)(klocal * D + chunk * 8) * 2u;
+    dma_key[i] = klocal;
+    dma_col[i] = chunk * 8;
   }
   const __amdgpu_buffer_rsrc_t rsrc_dma = dma_v ? rsrc_v : rsrc_k;
   lds_char* const lds = (lds_char*)smem;
   const int dma_lds0 = (dma_v ? G::kTileElems : 0) * 2 +
                        (w * G::kDmaPerWave - (dma_v ? G::kDmaPerTile : 0)) *
                            G::kRowsPerDma * D * 2;
+  // Paged: the sequence's block-table entries the tiles touch, staged in LDS
+  // after the ring (clamped into [0, num_blocks)).
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* const bt_s = (lds_int*)(lds + kStages * G::kStageElems * 2);
+  if constexpr (PAGED) {
+    const int nblk = no_keys ? 0 : min((kv_end + bs - 1) / bs, maxb);
+    for (int i = tid; i < nblk; i += kThreads)
+      bt_s[i] = min(max(block_table[(size_t)b * maxb + i], 0), num_blocks - 1);
+    __syncthreads();
+  }
+  const uint16_t* const cache_dma = dma_v ? V : K;
   auto issue_tile = [&](int t, int st) {
-    const uint32_t tile_off = (uint32_t)((t * kBc - key_lo) * D * 2);
     lds_char* dst = lds + st * G::kStageElems * 2 + dma_lds0;
+    if constexpr (PAGED) {
+      // Each row through the table; rows past the keys this workgroup needs
+      // repeat its last key (masked later) so no address leaves the cache.
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerWave; ++i)
-      dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D * 2);
+      for (int i = 0; i < G::kDmaPerWave; ++i) {
+        int tok = t * kBc + dma_key[i];
+        tok = tok < kv_end ? tok : kv_end - 1;
+        const int blk = bs_shift >= 0 ? tok >> bs_shift : tok / bs;
+        const size_t row = (size_t)bt_s[blk] * (size_t)bs + (size_t)(tok - blk * bs);
+        gdma16(cache_dma + (row * Hkv + hkv) * D + dma_col[i], dst + i * G::kRowsPerDma * D * 2);
+      }
+    } else {
+      const uint32_t tile_off = (uint32_t)((t * kBc - key_lo) * D * 2);
+#pragma unroll
+      for (int i = 0; i < G::kDmaPerWave; ++i)
+        dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D * 2);
+    }
   };
 
 #pragma unroll
@@ -290,8 +332,9 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
     const int j0 = t * kBc;
     // Whole wave above the causal diagonal, or wholly padding: nothing to add.
-    const bool wave_idle = (CAUSAL && j0 > wq0 + kQPerWave - 1) ||
-                           (RAGGED && wq0 + kQPerWave - 1 < pad);
+    const bool wave_idle = (CAUSAL && j0 > wq0 + qoff + kQPerWave - 1) ||
+                           (RAGGED && wq0 + kQPerWave - 1 < pad) ||
+                           (PAGED && wq0 + qoff + kQPerWave - 1 < 0);
     if (!wave_idle) {
       const lds_char* Ks = lds + st * G::kStageElems * 2;
       const lds_char* Vs = Ks + G::kTileElems * 2;
@@ -340,7 +383,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
       // Mask only tiles that straddle the diagonal, the pad or the end of K
       // (a real branch: most tiles need no mask at all).
-      const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0) || (j0 + kBc > key_hi) ||
+      const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0 + qoff) || (j0 + kBc > key_hi) ||
                              (j0 < key_lo);
       if (__builtin_expect(need_mask, 0)) {
 #pragma unroll
@@ -352,7 +395,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
             const bool kbad = key >= key_hi || key < key_lo;
 #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-              const bool bad = kbad || (CAUSAL && key > qrow[nt]);
+              const bool bad = kbad || (CAUSAL && key > qrow[nt] + qoff);
               sacc[mt][nt][i] = bad ? -__builtin_inff() : sacc[mt][nt][i];
             }
           }
@@ -587,21 +630,29 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <class T, int D, bool C, bool R, bool P>
+// Largest block table a paged launch stages in LDS (after the K/V ring).
+constexpr int kMaxPagedBlocks = 16384;
+
+template <class T, int D, bool C, bool R, bool P, bool PG>
 static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
   const int q_tiles = (a.n + kBr - 1) / kBr;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
-  const size_t lds = kStages * G::kStageElems * sizeof(uint16_t);
+  const size_t ring = kStages * G::kStageElems * sizeof(uint16_t);
+  const size_t lds = PG ? ring + (size_t)a.max_blocks * sizeof(int32_t) : ring;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R, P>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R, P, PG>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(PG ? ring + kMaxPagedBlocks * sizeof(int32_t) : ring));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P>), dim3((unsigned)total), dim3(kThreads), lds,
+  const int bs = PG ? a.block_size : 1;
+  const int shift = (PG && (bs & (bs - 1)) == 0) ? __builtin_ctz((unsigned)bs) : -1;
+  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P, PG>), dim3((unsigned)total), dim3(kThreads), lds,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.o_f32, a.lse, a.seq_lens,
                      a.heads_q, a.heads_q / a.heads_kv, a.n, a.m, a.key_begin, a.key_end,
-                     q_tiles, (int)total, a.scale * kLog2e);
+                     q_tiles, (int)total, a.scale * kLog2e, a.block_table, bs, shift,
+                     a.max_blocks, a.num_blocks);
   return hipGetLastError();
 }
 
@@ -619,10 +670,15 @@ static hipError_t launch_f32(const FwdArgs& a) {
 
 template <class T, int D, bool P>
 static hipError_t dispatch_mask(const FwdArgs& a) {
+  if (a.paged)  // paged chunks: no left padding, full key range
+    return a.causal ? launch_mfma<T, D, true, false, false, true>(a)
+                    : launch_mfma<T, D, false, false, false, true>(a);
   const bool r = a.seq_lens != nullptr;
   if (a.causal)
-    return r ? launch_mfma<T, D, true, true, P>(a) : launch_mfma<T, D, true, false, P>(a);
-  return r ? launch_mfma<T, D, false, true, P>(a) : launch_mfma<T, D, false, false, P>(a);
+    return r ? launch_mfma<T, D, true, true, P, false>(a)
+             : launch_mfma<T, D, true, false, P, false>(a);
+  return r ? launch_mfma<T, D, false, true, P, false>(a)
+           : launch_mfma<T, D, false, false, P, false>(a);
 }
 
 template <int D, bool P>
@@ -640,6 +696,8 @@ static hipError_t dispatch_dtype(const FwdArgs& a) {
     return a.d == 128 ? dispatch_mask<F16, 128, P>(a) : dispatch_mask<F16, 64, P>(a);
   return a.d == 128 ? dispatch_f32<128, P>(a) : dispatch_f32<64, P>(a);
 }
+
+int max_paged_blocks() { return kMaxPagedBlocks; }
 
 long long fwd_grid_size(int dtype, int batch, int heads_q, int n) {
   const int rows = dtype == 0 ? kF32Rows : kBr;

@@ -43,6 +43,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_partial.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    ctypes.c_float, _c_int, _c_void_p, _c_int, _c_int, _c_void_p]
+    lib.fa_paged_prefill.restype = _c_int
+    lib.fa_paged_prefill.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                     _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, _c_int, ctypes.c_float, _c_int, _c_void_p,
+                                     _c_void_p]
     lib.fa_merge.restype = _c_int
     lib.fa_merge.argtypes = [_c_int, _c_void_p, _c_void_p, _c_int, ctypes.c_longlong, _c_int,
                              _c_void_p, _c_void_p, _c_void_p]
@@ -219,6 +224,44 @@ def merge(o_parts, lse_parts, out_dtype=None, out=None, lse_out=None, want_lse: 
     check(lib.fa_merge(_dtype_code(out), _ptr(o_parts), _ptr(lse_parts), P, rows, dv, _ptr(out),
                        _ptr(lse_out), _stream(stream)))
     return (out, lse_out) if lse_out is not None else out
+
+
+def paged_prefill(q, k_cache, v_cache, block_table, seq_lens, block_size: int | None = None,
+                  scale: float | None = None, causal: bool = True, out=None, stream=None):
+    """A chunk of n query tokens per sequence over a paged cache that holds the
+    chunk's keys too: q [S, Hq, n, d] (row i is token seq_lens[s] - n + i);
+    k_cache [NB, bs, Hkv, d]; v_cache [NB, bs, Hkv, dv]; block_table int32
+    [S, max_blocks]; seq_lens int32 [S] total lengths.  Returns [S, Hq, n, dv]."""
+    import torch
+    lib = load_library()
+    dev = q.device
+    _require(q, "q", 4, dev)
+    _require(k_cache, "k_cache", 4, dev)
+    _require(v_cache, "v_cache", 4, dev)
+    _require(block_table, "block_table", 2, dev)
+    _require(seq_lens, "seq_lens", 1, dev)
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q, k_cache, v_cache must share a dtype")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    S, Hq, n, d = q.shape
+    NB, bs, Hkv, dk = k_cache.shape
+    dv = v_cache.shape[3]
+    if block_size is None:
+        block_size = bs
+    if bs != block_size or dk != d or tuple(v_cache.shape[:3]) != (NB, bs, Hkv):
+        raise ValueError("cache shapes do not match q / block_size")
+    if block_table.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_table / seq_lens batch mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((S, Hq, n, dv), dtype=q.dtype, device=dev)
+    check(lib.fa_paged_prefill(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv, n, d,
+                               dv, NB, block_table.shape[1], float(scale), 1 if causal else 0,
+                               _ptr(out), _stream(stream)))
+    return out
 
 
 def paged_decode_workspace_size(num_seqs, heads_q, heads_kv, dv, max_blocks_per_seq,

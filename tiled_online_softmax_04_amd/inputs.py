@@ -226,6 +226,27 @@ def make_decode(w: Decode, seq_lens=None) -> dict:
             "seq_lens": seq_lens.astype(np.int32), "num_blocks": NBa}
 
 
+def make_paged_chunk(w: Decode, n: int, seq_lens=None) -> dict:
+    """make_decode's cache, block table and lengths, with a chunk of n query
+    tokens per sequence, q [S, Hq, n, d], drawn from a second stream (seed + 1)
+    in place of the single decode token."""
+    x = make_decode(w, seq_lens)
+    rng = np.random.default_rng(w.seed + 1)
+    x["q"] = store(_normals(rng, (w.num_seqs, w.Hq, n, w.d)), w.dtype)
+    return x
+
+
+def paged_prefill_flops(seq_lens, n: int, Hq: int, d: int, dv: int, causal: bool = True) -> float:
+    """(2d + 2dv) per (query, allowed key) pair of a chunk of n rows at the end
+    of each sequence."""
+    pairs = 0
+    for L in np.asarray(seq_lens, dtype=np.int64):
+        L = int(L)
+        for i in range(max(0, n - L), n):
+            pairs += (L - n + i + 1) if causal else L
+    return float(pairs) * Hq * (2 * d + 2 * dv)
+
+
 def prefill_flops(w: Prefill, seq_lens=None) -> float:
     """Algorithmic FLOPs: 2*d + 2*dv per unmasked (query, key) pair."""
     per_pair = 2 * w.d + 2 * w.dv
