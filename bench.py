@@ -329,7 +329,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fa_fwd_mfma<BF16,128,false,false,false> (non-causal, no padding, full key range)",
+                     "kernel": "fa_fwd_mfma<BF16,128,false,false,false,false> (non-causal, no padding, full key range, contiguous)",
                      "avg_launch_ms": round(float(pre_ms.mean()), 5)},
         "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1),
