@@ -36,7 +36,10 @@ namespace fa {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecChunk = 16;          // tokens per wave step
+#ifndef FA_DECODE_CHUNK
+#define FA_DECODE_CHUNK 16
+#endif
+constexpr int kDecChunk = FA_DECODE_CHUNK;  // tokens per wave step
 #ifndef FA_DECODE_SPLIT
 #define FA_DECODE_SPLIT 512
 #endif
@@ -169,7 +172,8 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
       }
     }
     // Rare: raise the wave-uniform running max to the chunk max.
-    if (__any(raise)) {
+    if (__builtin_expect(__any(raise), 0)) {
+      asm volatile("" ::: "memory");  // a real branch, not a speculated rescale
 #pragma unroll
       for (int g = 0; g < GW; ++g) {
         float mx = s[g][0];

@@ -418,7 +418,10 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       // Raise the running max only when the tile beats it by more than kSlack
       // (wave-uniform branch).  Weights are then at most 2^kSlack, and acc and
       // l always share the same m, so O = acc / l is unchanged.
-      if (__any(raise)) {
+      if (__builtin_expect(__any(raise), 0)) {
+        // A real branch: without the barrier the compiler executes the
+        // rescale on every tile with alpha = 1.
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           const float m_new = fmaxf(m_run[nt], mx[nt]);
