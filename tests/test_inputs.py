@@ -110,3 +110,38 @@ def test_paged_prefill_flops_closed_form():
     assert gen.paged_prefill_flops([L], n, 2, 64, 64) == pairs * 2 * (4 * 64)
     assert gen.paged_prefill_flops([L], n, 1, 64, 64, causal=False) == n * L * 4 * 64
     assert gen.paged_prefill_flops([3], 5, 1, 1, 1) == (1 + 2 + 3) * 4  # rows before 0 skipped
+
+
+def test_e4m3_rounding_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32) * s
+                        for s in (0.003, 0.3, 30.0, 150.0)])
+    x = np.clip(x, -448, 448)
+    ours = gen.f32_to_e4m3(x)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_e4m3_ties_and_saturation():
+    # halfway cases go to the even mantissa; beyond 448 saturates
+    x = np.array([1.0625, 1.1875, 272.0, 2.0 ** -10, 3 * 2.0 ** -10, 464.0, 1000.0, -1e9,
+                  0.0, -0.0], np.float32)
+    want = [0x38, 0x3A, 0x78, 0x00, 0x02, 0x7E, 0x7E, 0xFE, 0x00, 0x80]
+    assert gen.f32_to_e4m3(x).tolist() == want
+
+
+def test_fp8_prefill_per_tensor_scaling_and_poison():
+    w = gen.Prefill("t", "fp8", 2, 4, 2, 40, 40, 64, 64, True, seed=9, ragged=(5, 40))
+    a, b = gen.make_prefill(w), gen.make_prefill(w)
+    for key in ("q", "k", "v", "seq_lens"):
+        assert np.array_equal(a[key], b[key])
+    assert a["q"].dtype == np.uint8 and a["k"].shape == (2, 2, 40, 64)
+    for name in ("q", "k", "v"):
+        d = a[name + "_descale"]
+        assert d == float(np.float32(d)) and d > 0
+        codes = a[name]
+        live = np.concatenate([codes[bi, :, p:].ravel() for bi, p in enumerate(a["pads"])])
+        # the largest real magnitude maps to (about) the top code, 448
+        assert (live & 0x7F).max() in (0x7E, 0x7D)
+        for bi, p in enumerate(a["pads"]):
+            assert np.all(codes[bi, :, :p] == gen.E4M3_NAN)

@@ -13,6 +13,9 @@ Recipe (every workload):
     overflow experiment of the 10100.com article, section 4);
   * storage casts are round-to-nearest-even: float32 -> bfloat16 by bit
     arithmetic, float32 -> float16 by numpy's cast.
+  * FP8 ("fp8": OCP E4M3, the e4m3fn encoding) is stored per tensor: the
+    float32 draws are divided by descale = amax / 448 (a float32) and rounded
+    to nearest-even E4M3 codes (uint8); the descale travels with the codes.
 Padding rows of a left-padded batch, cache slots past a sequence's length and
 unused block-table columns hold poison (NaN / -1) so that a kernel that reads
 them is caught.
@@ -24,10 +27,12 @@ import math
 
 import numpy as np
 
-DTYPES = ("f32", "f16", "bf16")
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPES = ("f32", "f16", "bf16", "fp8")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
 
 BF16_NAN = np.uint16(0x7FC0)
+E4M3_NAN = np.uint8(0x7F)
+E4M3_MAX = 448.0
 
 
 # --------------------------------------------------------------------------
@@ -68,9 +73,41 @@ def to_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(stored).astype(np.float64)
 
 
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to E4M3 codes (uint8), nearest-even, saturating
+    at +-448 (the largest finite E4M3 value).  Normal codes are
+    sign | (e + 7) << 3 | mantissa for |x| = (1 + mantissa / 8) * 2^e,
+    e in [-6, 8]; below 2^-6 the codes are subnormal, |x| = mantissa * 2^-9."""
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    # binade exponent of a (normal range), clamped to the subnormal binade
+    _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    steps = np.rint(a / np.ldexp(1.0, e - 3))  # multiples of the code spacing
+    # steps in [8, 16] for normals (16: rounded up into the next binade),
+    # [0, 8] in the subnormal binade (8: the smallest normal)
+    up = steps >= 16
+    e = np.where(up, e + 1, e)
+    steps = np.where(up, 8, steps).astype(np.int64)
+    normal = steps >= 8
+    code = np.where(normal, ((e + 7) << 3) | (steps - 8), steps)
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def quantize_e4m3(x32: np.ndarray) -> tuple[np.ndarray, float]:
+    """Per-tensor FP8 storage: (codes, descale) with descale = amax / 448 as a
+    float32 and codes = E4M3(x / descale); x ~= descale * decode(codes)."""
+    amax = float(np.max(np.abs(x32))) if x32.size else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    return f32_to_e4m3(np.asarray(x32, dtype=np.float64) / descale), descale
+
+
 def poison_value(dtype: str):
     if dtype == "bf16":
         return BF16_NAN
+    if dtype == "fp8":
+        return E4M3_NAN
     return np.nan
 
 
@@ -128,6 +165,8 @@ WORKLOADS = {
                            seed=3, ragged=(1024, 8192)),
     "cfg4": Decode("cfg4", "bf16", 64, 32, 8, 128, 128, 16, 512, 8192, 512, seed=4),
     "cfg5": Prefill("cfg5", "f16", 1, 16, 16, 16384, 16384, 128, 128, True, seed=5, hot=10.0),
+    # the bf16 2048-token prefill with FP8 (E4M3) storage
+    "cfg2_fp8": Prefill("cfg2_fp8", "fp8", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
 }
 
 
@@ -155,15 +194,25 @@ def make_prefill(w: Prefill) -> dict:
         lo, hi = w.ragged
         seq_lens = rng.integers(lo, hi, size=w.B, endpoint=True).astype(np.int32)
         pads = (w.n - seq_lens).astype(np.int64)
-    q, k, v = store(q32, w.dtype), store(k32, w.dtype), store(v32, w.dtype)
+    out = {"seq_lens": seq_lens, "pads": pads}
+    if w.dtype == "fp8":
+        # per-tensor scaling over the real (non-padding) entries
+        for name, x32 in (("q", q32), ("k", k32), ("v", v32)):
+            if pads is not None:
+                for b, p in enumerate(pads):
+                    x32[b, :, :p] = 0.0
+            codes, descale = quantize_e4m3(x32)
+            out[name], out[name + "_descale"] = codes, descale
+    else:
+        out["q"], out["k"], out["v"] = store(q32, w.dtype), store(k32, w.dtype), store(v32, w.dtype)
     del q32, k32, v32
     if pads is not None:
         pv = poison_value(w.dtype)
         for b, p in enumerate(pads):
-            q[b, :, :p] = pv
-            k[b, :, :p] = pv
-            v[b, :, :p] = pv
-    return {"q": q, "k": k, "v": v, "seq_lens": seq_lens, "pads": pads}
+            out["q"][b, :, :p] = pv
+            out["k"][b, :, :p] = pv
+            out["v"][b, :, :p] = pv
+    return out
 
 
 def make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, dv, seed, hot=1.0, lens=None,
