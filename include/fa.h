@@ -110,6 +110,31 @@ fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* 
                          int key_begin, int key_end, void* stream);
 
 /*
+ * fa_fwd_fp8 -- fa_fwd on FP8 inputs.  The S12 chapter's production list
+ * names FP8 support only as something FlashAttention-3 added on Hopper; here
+ * q, k and v are OCP 8-bit floating point E4M3 codes ("e4m3fn": bias 7, no
+ * infinities, 0x7F and 0xFF are NaN, largest finite value 448), one byte per
+ * element, each tensor with a float32 descale factor:
+ *
+ *   real q = q_descale * E4M3(q), real k = k_descale * E4M3(k),
+ *   real v = v_descale * E4M3(v),
+ *   O = softmax(scale * real_q real_k^T [+ mask]) real_v,
+ *
+ * written as out_dtype (FA_DTYPE_F32, F16 or BF16; RNE).  Shapes, head
+ * grouping, scale, causal and seq_lens mean what they mean in fa_fwd; tensor
+ * pointers must be 16-byte aligned.  Scores are exact code products summed in
+ * the matrix cores; the softmax weights enter the P.V product rounded to E4M3
+ * (about 2^-4 relative each), the one deliberate loss of this path.
+ * FA_ERR_INVALID additionally for descales that are not finite and > 0, or
+ * whose product with scale underflows float32.  Limits: d == dv in {64, 128}
+ * (else FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, fa_dtype out_dtype,
+                     int batch, int heads_q, int heads_kv, int n, int m, int d, int dv,
+                     float scale, float q_descale, float k_descale, float v_descale, int causal,
+                     const int32_t* seq_lens, void* stream);
+
+/*
  * fa_merge -- combine attention pieces over disjoint key ranges (the S12
  * exercise 1 rescale applied to whole pieces): with L = max_s lse_s and
  * w_s = exp(lse_s - L),

@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_partial", "fa_last_error", "fa_merge",
+    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_fwd_partial", "fa_last_error",
+                                    "fa_merge",
                                     "fa_paged_decode", "fa_paged_decode_workspace_size",
                                     "fa_paged_prefill", "fa_status_string"]
 
@@ -87,6 +88,41 @@ def test_fwd_empty_work_is_ok_without_pointers(lib):
     assert fwd(lib, q=None, k=None, v=None, o=None, B=0) == fa.FA_OK
     assert fwd(lib, q=None, k=None, v=None, o=None, n=0, m=0) == fa.FA_OK
     assert lib.fa_last_error().decode() == ""
+
+
+def fwd8(lib, q=P, k=P, v=P, o=P, out=2, B=1, Hq=2, Hkv=2, n=128, m=128, d=128, dv=128,
+         scale=0.088, qd=0.01, kd=0.01, vd=0.01, causal=0, seq_lens=None):
+    return lib.fa_fwd_fp8(q, k, v, o, out, B, Hq, Hkv, n, m, d, dv, scale, qd, kd, vd, causal,
+                          seq_lens, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=3), fa.FA_ERR_INVALID),
+    (dict(B=-1), fa.FA_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(causal=1, m=64), fa.FA_ERR_INVALID),
+    (dict(seq_lens=P, m=64), fa.FA_ERR_INVALID),
+    (dict(scale=0.0), fa.FA_ERR_INVALID),
+    (dict(qd=0.0), fa.FA_ERR_INVALID),
+    (dict(kd=-1.0), fa.FA_ERR_INVALID),
+    (dict(vd=float("nan")), fa.FA_ERR_INVALID),
+    (dict(vd=float("inf")), fa.FA_ERR_INVALID),
+    (dict(qd=1e-30, kd=1e-30), fa.FA_ERR_INVALID),   # scale * qd * kd underflows
+    (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=128, dv=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=None), fa.FA_ERR_INVALID),
+    (dict(v=MISALIGNED), fa.FA_ERR_INVALID),
+    (dict(n=1 << 24, m=1 << 24), fa.FA_ERR_INVALID),
+])
+def test_fwd_fp8_rejects_before_launch(lib, kw, code):
+    assert fwd8(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fwd_fp8_empty_work_is_ok(lib):
+    assert fwd8(lib, q=None, k=None, v=None, o=None, B=0) == fa.FA_OK
+    # descales are checked even when there is nothing to compute
+    assert fwd8(lib, q=None, k=None, v=None, o=None, B=0, vd=0.0) == fa.FA_ERR_INVALID
 
 
 def dec(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, dv=128, NB=64,

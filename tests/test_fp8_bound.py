@@ -1,0 +1,65 @@
+"""The FP8 error bound (tests/fp8_bound.py) against a CPU model of the FP8
+path's arithmetic: exact code-product scores, the lazily raised running max
+over 64-key tiles (slack 8), weights rounded to E4M3, float64 sums, the
+v_descale / l epilogue and a bfloat16 output.  The model must stay inside the
+bound (so the bound is not too tight for the arithmetic it describes) and use
+a fair share of it (so it is not vacuous)."""
+import numpy as np
+import pytest
+
+import oracle
+from tiled_online_softmax_04_amd import inputs as gen
+
+import fp8_bound
+
+
+def model_head(q8, k8, v8, qd, kd, vd, scale, causal, pad):
+    """FP8 path of one head, modelled on the CPU (float64 sums)."""
+    qc, kc, vc = (oracle.e4m3_to_f64(x) for x in (q8, k8, v8))
+    n, m = qc.shape[0], kc.shape[0]
+    c = np.float32(scale * np.float32(qd) * np.float32(kd) * np.log2(np.e))
+    out = np.zeros((n, vc.shape[1]))
+    for i in range(pad, n):
+        m_run, l, acc = -1e30, 0.0, np.zeros(vc.shape[1])
+        hi = i + 1 if causal else m
+        for j0 in range((pad // 64) * 64, hi, 64):
+            keys = np.arange(max(j0, pad), min(j0 + 64, hi))
+            if keys.size == 0:
+                continue
+            t = (np.float32(kc[keys] @ qc[i]) * c).astype(np.float64)
+            mx = t.max()
+            if mx > m_run + 8:
+                alpha = 2.0 ** (m_run - mx)
+                acc, l, m_run = acc * alpha, l * alpha, mx
+            p = oracle.e4m3_to_f64(gen.f32_to_e4m3(np.float32(2.0 ** (t - m_run))))
+            acc = acc + p @ vc[keys]
+            l += p.sum()
+        o32 = np.float32(acc * (np.float32(vd) / np.float32(l)))
+        out[i] = gen.bf16_bits_to_f64(gen.f32_to_bf16_bits(o32))
+    return out
+
+
+@pytest.mark.parametrize("name,causal,hot,lens", [
+    ("noncausal", False, 1.0, None),
+    ("causal_hot", True, 10.0, None),
+    ("causal_leftpad", True, 1.0, [150, 61]),
+])
+def test_model_inside_bound(name, causal, hot, lens):
+    x = gen.make_prefill_custom("fp8", 2, 1, 1, 150, 150, 64, 64, seed=11, hot=hot, lens=lens)
+    scale = float(np.float32(1 / 8.0))
+    ratios = []
+    for b in range(2):
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        got = model_head(x["q"][b, 0], x["k"][b, 0], x["v"][b, 0], x["q_descale"],
+                         x["k_descale"], x["v_descale"], scale, causal, pad)
+        q = oracle.dequantize(x["q"][b, 0], x["q_descale"])
+        k = oracle.dequantize(x["k"][b, 0], x["k_descale"])
+        v = oracle.dequantize(x["v"][b, 0], x["v_descale"])
+        ref, B, sig = fp8_bound.head_bounds(q, k, v, scale, causal, pad)
+        ratio, rms_ratio = fp8_bound.check(got, ref, B, sig, f"{name} b={b}")
+        ratios.append(rms_ratio)
+    # the modelled error is a visible fraction of the predicted spread (on hot
+    # inputs the spread is dominated by the matrix-core score term, which the
+    # model leaves out)
+    if hot == 1.0:
+        assert max(ratios) > 0.1

@@ -1,0 +1,143 @@
+"""GPU parity of the FP8 prefill (fa_fwd_fp8) against the float64 oracle on
+the dequantized inputs (oracle.attention_fp8), through the C ABI.
+
+Bar: no tolerance for FP8 is given by the pages, so tests/fp8_bound.py derives
+one from the arithmetic (E4M3 weights, matrix-core sums, output rounding):
+every element within its rigorous bound, and the rms error within twice the
+predicted spread.  Inputs whose weights are exact in E4M3 (all scores equal:
+Q = 0) leave only the sums and the output rounding, and are held to that."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from tiled_online_softmax_04_amd import fa
+from tiled_online_softmax_04_amd import inputs as gen
+
+import fp8_bound
+from gpu_util import say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def out_dtype(name):
+    import torch
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[name]
+
+
+def run(x, causal, scale, out):
+    import torch
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x[t])).cuda() for t in ("q", "k", "v"))
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).cuda()
+    o = fa.fwd_fp8(q, k, v, x["q_descale"], x["k_descale"], x["v_descale"], scale=scale,
+                   causal=causal, seq_lens=sl, out_dtype=out_dtype(out))
+    torch.cuda.synchronize()
+    return to_f64(o, out)
+
+
+def real(x, t):
+    return oracle.dequantize(x[t], x[t + "_descale"])
+
+
+CASES = [
+    # name, out, B, Hq, Hkv, n, m, d, causal, hot, lens
+    ("noncausal_tail", "bf16", 2, 4, 4, 300, 300, 128, False, 1.0, None),
+    ("causal_333_f16", "f16", 1, 3, 3, 333, 333, 128, True, 1.0, None),
+    ("causal_hot", "bf16", 1, 2, 2, 520, 520, 128, True, 10.0, None),
+    ("causal_leftpad", "bf16", 4, 2, 2, 400, 400, 128, True, 1.0, [400, 1, 0, 137]),
+    ("noncausal_leftpad_f32", "f32", 3, 2, 2, 260, 260, 128, False, 1.0, [260, 64, 5]),
+    ("gqa_d64_causal", "bf16", 1, 8, 2, 200, 200, 64, True, 1.0, None),
+    ("n_ne_m_f32", "f32", 2, 2, 1, 100, 333, 128, False, 1.0, None),
+    ("d64_noncausal_f16", "f16", 1, 4, 4, 129, 129, 64, False, 1.0, None),
+    ("single_row", "bf16", 1, 1, 1, 1, 1, 128, True, 1.0, None),
+    ("single_key_d64", "bf16", 1, 2, 2, 70, 1, 64, False, 1.0, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_small(case):
+    name, out, B, Hq, Hkv, n, m, d, causal, hot, lens = case
+    say(f"[fp8] {name}")
+    x = gen.make_prefill_custom("fp8", B, Hq, Hkv, n, m, d, d,
+                                seed=zlib.crc32(name.encode()) % 1000, hot=hot, lens=lens)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = run(x, causal, scale, out)
+    q, k, v = real(x, "q"), real(x, "k"), real(x, "v")
+    g = Hq // Hkv
+    ref = np.zeros_like(got)
+    B_ = np.zeros_like(got)
+    sig = np.zeros_like(got)
+    for b in range(B):
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        for h in range(Hq):
+            ref[b, h], B_[b, h], sig[b, h] = fp8_bound.head_bounds(
+                q[b, h], k[b, h // g], v[b, h // g], scale, causal, pad)
+    # the bound's reference is the oracle's definition on the same inputs
+    full = oracle.attention_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"],
+                                x["v_descale"], scale, causal, x["pads"])
+    assert np.allclose(ref, full, rtol=0, atol=1e-12)
+    fp8_bound.check(got, ref, B_, sig, name, say)
+    if x["pads"] is not None:
+        for b, p in enumerate(x["pads"]):
+            assert np.all(got[b, :, :p] == 0)
+
+
+@pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (True, [300, 77])])
+def test_fp8_equal_scores_give_means(causal, lens):
+    """Q = 0: every allowed key weighs exactly 1 in E4M3, so O is the mean of V
+    over the allowed keys (prefix means when causal), up to the matrix-core
+    sums (2^-12 of sum |v|, below 2^-10 max |v| per output) and the bfloat16
+    output (2^-9)."""
+    say(f"[fp8] Q = 0 causal={causal} lens={lens}")
+    x = gen.make_prefill_custom("fp8", 2, 2, 2, 300, 300, 128, 128, seed=21, lens=lens)
+    live = x["q"] != gen.E4M3_NAN
+    x["q"] = np.where(live, np.uint8(0), x["q"]).astype(np.uint8)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    got = run(x, causal, scale, "bf16")
+    ref = oracle.attention_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"],
+                               x["v_descale"], scale, causal, x["pads"])
+    vmax = np.nanmax(np.abs(real(x, "v")))   # padding rows hold NaN codes
+    tol = 2.0 ** -8 * np.abs(ref) + 2.0 ** -10 * vmax
+    err = np.abs(got - ref)
+    say(f"  max_abs={err.max():.3e} worst err/tol={(err / tol).max():.3f}")
+    assert np.all(np.isfinite(got)) and np.all(err <= tol)
+
+
+def test_fp8_constant_values():
+    """V constant: O equals it for every row with keys, whatever the weights."""
+    import torch
+    say("[fp8] V constant")
+    x = gen.make_prefill_custom("fp8", 1, 2, 2, 256, 256, 128, 128, seed=5, hot=10.0)
+    x["v"] = np.full_like(x["v"], 0x40)          # E4M3 2.0
+    scale = float(np.float32(1 / np.sqrt(128)))
+    got = run(x, True, scale, "f32")
+    want = 2.0 * float(np.float32(x["v_descale"]))
+    err = np.abs(got - want)
+    say(f"  max_abs={err.max():.3e}")
+    assert np.all(err <= 2.0 ** -20 * want)
+
+
+def test_fp8_full_size_sampled():
+    """The 2048-token bf16 workload stored as FP8: the whole output finite,
+    sampled rows within the bound against the oracle."""
+    import torch
+    w = gen.WORKLOADS["cfg2_fp8"]
+    say("[fp8] cfg2_fp8 full size, sampled rows")
+    x = gen.make_prefill(w)
+    q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
+    o = fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all())
+    rng = np.random.default_rng(13)
+    samples = [(0, 0), (w.B - 1, w.Hq - 1)] + \
+        [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(6)]
+    for b, h in samples:
+        rows = np.sort(rng.choice(w.n, size=8, replace=False))
+        rows[0] = 0 if (b, h) == (0, 0) else rows[0]
+        q = oracle.dequantize(x["q"][b, h, rows], x["q_descale"])
+        k = oracle.dequantize(x["k"][b, h], x["k_descale"])
+        v = oracle.dequantize(x["v"][b, h], x["v_descale"])
+        ref, B_, sig = fp8_bound.row_bounds(q, rows, k, v, w.scale)
+        got = to_f64(o[b, h, torch.from_numpy(rows).cuda()], "bf16")
+        fp8_bound.check(got, ref, B_, sig, f"cfg2_fp8 b={b} h={h} rows={rows.tolist()}", say)

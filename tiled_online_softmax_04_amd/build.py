@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["fa_api.hip", "fa_prefill.hip", "fa_decode.hip", "fa_merge.hip"]
+SOURCES = ["fa_api.hip", "fa_prefill.hip", "fa_prefill_fp8.hip", "fa_decode.hip", "fa_merge.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions stay off: the compiler must not form v_pk_*_f32.

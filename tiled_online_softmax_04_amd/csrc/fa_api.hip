@@ -100,6 +100,35 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
   return FA_OK;
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, fa_dtype out_dtype,
+                     int batch, int heads_q, int heads_kv, int n, int m, int d, int dv,
+                     float scale, float q_descale, float k_descale, float v_descale, int causal,
+                     const int32_t* seq_lens, void* stream) {
+  g_last_error[0] = '\0';
+  // Shape, pointer and scale checks as fa_fwd (the bf16 kernel's row counts
+  // stand in for the element size, which the checks do not use).
+  bool empty;
+  fa_status s = check_fwd(out_dtype, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
+                          causal, seq_lens, &empty);
+  if (s != FA_OK) return s;
+  const float ds[3] = {q_descale, k_descale, v_descale};
+  for (float x : ds)
+    if (!(x > 0.f) || !isfinite(x))
+      return fail(FA_ERR_INVALID, "descales must be finite and > 0 (got %g, %g, %g)",
+                  (double)q_descale, (double)k_descale, (double)v_descale);
+  const double c = (double)scale * q_descale * k_descale * 1.4426950408889634;
+  if (!(c >= 1.1754943508222875e-38) || !(c < 3.4e38))
+    return fail(FA_ERR_INVALID, "scale * q_descale * k_descale out of float32 range (%g)", c);
+  if (empty) return FA_OK;
+  const long long grid = fa::fwd_fp8_grid_size(batch, heads_q, n);
+  if (grid >= (1LL << 31)) return fail(FA_ERR_INVALID, "grid too large (%lld)", grid);
+  fa::Fp8Args a{(int)out_dtype, q, k, v, o, batch, heads_q, heads_kv, n, m, d, scale,
+                q_descale, k_descale, v_descale, causal ? 1 : 0, seq_lens, stream};
+  const hipError_t e = fa::launch_fwd_fp8(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_fwd_fp8 launch");
+  return FA_OK;
+}
+
 fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* v, float* o,
                          float* lse, int batch, int heads_q, int heads_kv, int n, int m, int d,
                          int dv, float scale, int causal, const int32_t* seq_lens,

@@ -34,6 +34,23 @@ struct FwdArgs {
   int block_size, max_blocks, num_blocks;
 };
 
+// FP8 prefill: q, k, v are E4M3 codes [batch, heads, rows, d] with one
+// descale factor each; o is out_dtype (0 f32, 1 f16, 2 bf16).
+struct Fp8Args {
+  int out_dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int batch, heads_q, heads_kv, n, m, d;
+  float scale, q_descale, k_descale, v_descale;
+  int causal;
+  const int32_t* seq_lens;
+  void* stream;
+};
+long long fwd_fp8_grid_size(int batch, int heads_q, int n);
+hipError_t launch_fwd_fp8(const Fp8Args& a);
+
 // Merge of key-range pieces: o_parts [parts, rows, dv] and lse_parts
 // [parts, rows] (float32) into o [rows, dv] of out_dtype and, if non-null,
 // lse_out [rows].

@@ -43,6 +43,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_partial.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                    _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    ctypes.c_float, _c_int, _c_void_p, _c_int, _c_int, _c_void_p]
+    lib.fa_fwd_fp8.restype = _c_int
+    lib.fa_fwd_fp8.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                               ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                               _c_int, _c_void_p, _c_void_p]
     lib.fa_paged_prefill.restype = _c_int
     lib.fa_paged_prefill.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                      _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -162,6 +167,36 @@ def _check_qkv(q, k, v, seq_lens):
         if seq_lens.dtype != torch.int32 or seq_lens.shape[0] != B:
             raise ValueError("seq_lens must be int32 [B]")
     return B, Hq, Hkv, n, m, d, v.shape[3]
+
+
+def fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+            scale: float | None = None, causal: bool = False, seq_lens=None,
+            out_dtype=None, out=None, stream=None):
+    """Attention on FP8 inputs: q, k, v hold E4M3 codes (torch.uint8 or
+    torch.float8_e4m3fn, shapes as ``fwd``); the real inputs are descale *
+    E4M3(code) per tensor.  O is out_dtype (default bfloat16).  scale defaults
+    to 1/sqrt(d)."""
+    import torch
+    lib = load_library()
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    for name, t_ in (("q", q), ("k", k), ("v", v)):
+        if t_.dtype not in (torch.uint8, fp8):
+            raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), "
+                             f"got {t_.dtype}")
+    qb, kb, vb = (t_ if t_.dtype == torch.uint8 else t_.view(torch.uint8) for t_ in (q, k, v))
+    B, Hq, Hkv, n, m, d, dv = _check_qkv(qb, kb, vb, seq_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, n, dv), dtype=out_dtype or torch.bfloat16, device=q.device)
+    else:
+        _require(out, "out", 4, q.device)
+        if tuple(out.shape) != (B, Hq, n, dv) or (out_dtype is not None and out.dtype != out_dtype):
+            raise ValueError("out has the wrong shape or dtype")
+    check(lib.fa_fwd_fp8(_ptr(qb), _ptr(kb), _ptr(vb), _ptr(out), _dtype_code(out), B, Hq, Hkv,
+                         n, m, d, dv, float(scale), float(q_descale), float(k_descale),
+                         float(v_descale), 1 if causal else 0, _ptr(seq_lens), _stream(stream)))
+    return out
 
 
 def fwd_partial(q, k, v, key_begin: int, key_end: int, scale: float | None = None,
