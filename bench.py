@@ -11,6 +11,9 @@ before timing starts.  Prints one JSON line:
   roofline  the prefill kernel against the bf16 dense MFMA peak
   decode    paged decode GB/s (algorithmic bytes) against HBM peak
   cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
+After the timed steps, the same prefill is also timed as four key-range pieces
+plus their merge, as a paged causal chunk over the decode cache, and with FP8
+(E4M3) inputs against the FP8 MFMA peak.
 """
 from __future__ import annotations
 
@@ -28,10 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_prefill.hip",
+                   "tiled_online_softmax_04_amd/csrc/fa_lds.h",
                    "tiled_online_softmax_04_amd/csrc/fa_common.h"]
+FP8_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_prefill_fp8.hip",
+               "tiled_online_softmax_04_amd/csrc/fa_lds.h",
+               "tiled_online_softmax_04_amd/csrc/fa_common.h"]
 DECODE_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_decode.hip",
                   "tiled_online_softmax_04_amd/csrc/fa_common.h"]
 
@@ -166,6 +174,43 @@ def time_paged_prefill(fa, wd, kc, vc, bt, sl, seq_lens, iters: int, n: int = 51
             "iters": iters}
 
 
+def time_fp8(fa, iters: int):
+    """The headline prefill with Q, K, V stored as FP8 E4M3 (per-tensor
+    descales) and a bf16 output; HIP events around each fa_fwd_fp8 call."""
+    import torch
+    from tiled_online_softmax_04_amd import inputs as gen
+    if iters <= 0:
+        return None
+    w = gen.WORKLOADS["cfg2_fp8"]
+    x = gen.make_prefill(w)
+    q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
+    out = torch.empty((w.B, w.Hq, w.n, w.dv), dtype=torch.bfloat16, device=q8.device)
+
+    def run():
+        fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"], scale=w.scale,
+                   out=out)
+
+    for _ in range(max(200, iters)):   # steady clocks after the other legs
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    tflops = gen.prefill_flops(w) / (ms * 1e-3) / 1e12
+    return {"workload": "the prefill above (B=4 H=32 n=m=2048 d=dv=128 non-causal) with Q, K, V "
+                        "stored as FP8 E4M3 with per-tensor descales, bf16 output",
+            "tflops": round(tflops, 2), "ms": round(ms, 5), "iters": iters,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
+                         "traffic": read_traffic("fa_fwd_fp8_cfg2_traffic.txt", FP8_SOURCES),
+                         "kernel": "fa_fwd_fp8<128,false,false,2> (non-causal, no padding, "
+                                   "bf16 out)"}}
+
+
 def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
     """Peak device memory of one attention head, beyond its inputs and output:
     the tiled library call against the plain three-step evaluation that keeps
@@ -217,8 +262,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--key-split-iters", type=int, default=30,
-                    help="timed runs of the key-split and paged-prefill variants after the step "
-                         "(0 skips them)")
+                    help="timed runs of the key-split, paged-prefill and FP8 variants after the "
+                         "step (0 skips them)")
     ap.add_argument("--peak-memory", type=int, default=1,
                     help="1: also report peak device memory, tiled vs naive, at n = 512, 2048, "
                          "8192 (0 skips it)")
@@ -299,6 +344,7 @@ def main():
 
     key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
     paged = time_paged_prefill(fa, wd, kc, vc, bt, sl, xd["seq_lens"], args.key_split_iters)
+    fp8 = time_fp8(fa, args.key_split_iters)
     mem = peak_memory(fa) if args.peak_memory else None
 
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
@@ -341,6 +387,7 @@ def main():
         "cpu_baseline": baseline,
         "key_split": key_split,
         "paged_prefill": paged,
+        "fp8": fp8,
         "peak_memory": mem,
     }
     print(json.dumps(out), flush=True)
