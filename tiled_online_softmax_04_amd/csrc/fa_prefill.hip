@@ -3,9 +3,11 @@
 // fa_fwd_mfma: bf16 / fp16 inputs.  One workgroup of 8 waves (two per SIMD)
 // owns 256 query rows of one (batch, head); each wave owns 32 of them and
 // keeps them resident in VGPRs as MFMA operands ("Q 常驻片上寄存器", 10100.com
-// section 7).  64-key K/V tiles stream through a ring of three LDS stages:
-// each wave moves its share of a tile with buffer loads that write LDS
-// directly (no VGPR round trip), two tiles ahead of the one being computed.
+// section 7).  64-key K/V tiles stream through a ring of LDS stages: each
+// wave moves its share of a tile with buffer loads that write LDS directly (no
+// VGPR round trip).  Two tiles are computed between barriers from one half of
+// a four-stage ring while the next two land in the other half (the paged form:
+// one tile per barrier, three stages, two tiles ahead).
 // Per tile the wave forms S^T = K Q^T with v_mfma_f32_32x32x16, applies the
 // online-softmax update of the same section (running max, rescale of the
 // history by exp(m_old - m_new), running sum) and accumulates O^T += V^T P^T
@@ -51,6 +53,17 @@ constexpr int kThreads = 64 * kWaves;
 // LDS ring of K/V tiles: tile t is computed while tiles t+1 .. t+kStages-1 land.
 constexpr int kStages = FA_PREFILL_STAGES;
 static_assert(kStages == 2 || kStages == 3, "ring depth");
+// Tiles computed between two barriers.  With more than one, the ring holds
+// 2 * kGroup stages: one half is computed while the next group lands in the
+// other half.  The paged form keeps one tile per barrier (its block table
+// shares LDS with the ring).
+#ifndef FA_PREFILL_GROUP
+#define FA_PREFILL_GROUP 2
+#endif
+constexpr int kGroup = FA_PREFILL_GROUP;
+constexpr int ring_stages(bool paged) {
+  return (!paged && kGroup > 1) ? 2 * kGroup : kStages;
+}
 
 template <int D>
 struct Geo {
@@ -110,6 +123,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     int m, int key_begin, int key_end, int q_tiles, int total, float c,
     const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks) {
   using G = Geo<D>;
+  constexpr int kGrp = PAGED ? 1 : kGroup;
+  constexpr int kRing = ring_stages(PAGED);
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -197,7 +212,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   // Paged: the sequence's block-table entries the tiles touch, staged in LDS
   // after the ring (clamped into [0, num_blocks)).
   typedef __attribute__((address_space(3))) int lds_int;
-  lds_int* const bt_s = (lds_int*)(lds + kStages * G::kStageElems * 2);
+  lds_int* const bt_s = (lds_int*)(lds + kRing * G::kStageElems * 2);
   if constexpr (PAGED) {
     const int nblk = no_keys ? 0 : min((kv_end + bs - 1) / bs, maxb);
     for (int i = tid; i < nblk; i += kThreads)
@@ -227,7 +242,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   };
 
 #pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
+  for (int i = 0; i < (kGrp > 1 ? kGrp : kStages - 1); ++i)
     if (t_begin + i < t_end) issue_tile(t_begin + i, i);
 
   // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive d.
@@ -267,13 +282,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   wait_vm_lgkm0<0>();
   bare_barrier();
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int it = t - t_begin;
-    const int st = it % kStages;
-    // Refill the stage read in the previous iteration with tile t+kStages-1.
-    const bool pre = t + kStages - 1 < t_end;
-    if (pre) issue_tile(t + kStages - 1, (it + kStages - 1) % kStages);
-
+  // One tile from ring stage st: scores, online softmax, P.V.
+  auto tile = [&](int t, int st) __attribute__((always_inline)) {
     const int j0 = t * kBc;
     // Whole wave above the causal diagonal, or wholly padding: nothing to add.
     const bool wave_idle = (CAUSAL && j0 > wq0 + qoff + kQPerWave - 1) ||
@@ -406,15 +416,38 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       wait_lgkm0();
       static_for<2, 4>([&](auto J) { mma_v(J, pb); });
     }
+  };
 
-    // This wave's part of tile t+1 has landed and its reads of stage st are
-    // done; after the barrier every wave may read t+1 and refill stage st.
-    if (kStages == 3 && pre) {
-      wait_vm_lgkm0<(kStages - 2) * G::kDmaPerWave>();  // tile t+2 may stay in flight
-    } else {
+  if constexpr (kGrp > 1) {
+    // kGrp tiles from one half of the ring while the next kGrp land in the
+    // other half; one barrier per group.
+    for (int t = t_begin; t < t_end; t += kGrp) {
+      const int it = t - t_begin;
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g)
+        if (t + kGrp + g < t_end) issue_tile(t + kGrp + g, (it + kGrp + g) % kRing);
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g)
+        if (t + g < t_end) tile(t + g, (it + g) % kRing);
       wait_vm_lgkm0<0>();
+      bare_barrier();
     }
-    bare_barrier();
+  } else {
+    for (int t = t_begin; t < t_end; ++t) {
+      const int it = t - t_begin;
+      // Refill the stage read in the previous iteration with tile t+kStages-1.
+      const bool pre = t + kStages - 1 < t_end;
+      if (pre) issue_tile(t + kStages - 1, (it + kStages - 1) % kStages);
+      tile(t, it % kStages);
+      // This wave's part of tile t+1 has landed and its reads of stage st are
+      // done; after the barrier every wave may read t+1 and refill stage st.
+      if (kStages == 3 && pre) {
+        wait_vm_lgkm0<(kStages - 2) * G::kDmaPerWave>();  // tile t+2 may stay in flight
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      bare_barrier();
+    }
   }
 
   // -------- epilogue: O = acc / l, zero for rows without keys --------
@@ -585,7 +618,7 @@ static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
   const int q_tiles = (a.n + kBr - 1) / kBr;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
-  const size_t ring = kStages * G::kStageElems * sizeof(uint16_t);
+  const size_t ring = ring_stages(PG) * G::kStageElems * sizeof(uint16_t);
   const size_t lds = PG ? ring + (size_t)a.max_blocks * sizeof(int32_t) : ring;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R, P, PG>),

@@ -7,8 +7,9 @@
 //
 // Shape: one workgroup of 8 waves (two per SIMD) owns 256 query rows of one
 // (batch, head); each wave keeps its 32 query rows in VGPRs for the whole key
-// loop.  64-key K/V tiles stream through a ring of three LDS stages filled by
-// buffer loads that write LDS directly, two tiles ahead of the one computed.
+// loop.  64-key K/V tiles stream through a four-stage LDS ring filled by
+// buffer loads that write LDS directly: two tiles are computed between
+// barriers while the next two land.
 // Both products run on v_mfma_f32_32x32x64_f8f6f4 (64 fp8 products per lane
 // per instruction, twice the bf16 rate):
 //   S^T = K Q^T: per 32-key block, d/64 MFMAs; K rows come from LDS (32
@@ -40,6 +41,13 @@ constexpr int kT8 = 64 * kW8;    // threads per workgroup
 constexpr int kBr8 = 32 * kW8;   // query rows per workgroup
 constexpr int kBc8 = 64;         // keys per tile
 constexpr int kStages8 = 3;      // LDS ring depth
+// Tiles computed between two barriers.  Two halve the barrier waits per
+// tile; the ring then holds four stages, two computed while two land.
+#ifndef FA8_GROUP
+#define FA8_GROUP 2
+#endif
+constexpr int kGroup8 = FA8_GROUP;
+constexpr int kRing8 = kGroup8 > 1 ? 2 * kGroup8 : kStages8;
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(8 * sizeof(uint32_t)))) uint32_t u32x8;
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     void* __restrict__ O, const int32_t* __restrict__ seq_lens, int Hq, int group, int n, int m,
     int q_tiles, int total, float c, float v_descale) {
   using G = Geo8<D>;
-  __shared__ __align__(16) uint8_t smem[kStages8 * G::kStageBytes];
+  __shared__ __align__(16) uint8_t smem[kRing8 * G::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
       dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D);
   };
 #pragma unroll
-  for (int i = 0; i < kStages8 - 1; ++i)
+  for (int i = 0; i < (kGroup8 > 1 ? kGroup8 : kStages8 - 1); ++i)
     if (t_begin + i < t_end) issue_tile(t_begin + i, i);
 
   // Queries as B operands of S^T = K Q^T: lane holds query ql, 32 consecutive
@@ -221,29 +229,35 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
   wait_vm_lgkm0<0>();
   bare_barrier();
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int it = t - t_begin;
-    const int st = it % kStages8;
-    const bool pre = t + kStages8 - 1 < t_end;
-    if (pre) issue_tile(t + kStages8 - 1, (it + kStages8 - 1) % kStages8);
-
+  // A whole wave above the causal diagonal, or wholly padding, skips a tile.
+  auto wave_idle = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * kBc8;
-    const bool wave_idle = (CAUSAL && j0 > wq0 + 31) || (RAGGED && wq0 + 31 < pad);
-    if (!wave_idle) {
-      const lds_char* Ks = lds + st * G::kStageBytes;
-      const lds_char* Vs = Ks + G::kTileBytes;
-
-      // S^T[key][query] for 64 keys: two 32-key blocks.
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    int all_pad = __builtin_amdgcn_readfirstlane(RAGGED && wq0 + 31 < pad);
+    // Loop-invariant when not causal; evaluated in the loop all the same, so
+    // that the compiler does not unswitch the loop on it (the second copy of
+    // the loop body spills).
+    asm volatile("" : "+s"(all_pad));
+    return (CAUSAL && j0 > wq0 + 31) || all_pad != 0;
+  };
+  // S^T[key][query] of tile t (ring stage st) for 64 keys: two 32-key blocks.
+  auto scores = [&](int st, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+    const lds_char* Ks = lds + st * G::kStageBytes;
+    sacc[0] = sacc[1] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < G::kQSteps; ++ks) {
-        const u32x8 a0 = cat(*(const lds_u32x4*)(Ks + k_off[ks][0]),
-                             *(const lds_u32x4*)(Ks + k_off[ks][1]));
-        const u32x8 a1 = cat(*(const lds_u32x4*)(Ks + k_off[ks][0] + 32 * D),
-                             *(const lds_u32x4*)(Ks + k_off[ks][1] + 32 * D));
-        sacc[0] = mfma_fp8(a0, qT[ks], sacc[0]);
-        sacc[1] = mfma_fp8(a1, qT[ks], sacc[1]);
-      }
+    for (int ks = 0; ks < G::kQSteps; ++ks) {
+      const u32x8 a0 = cat(*(const lds_u32x4*)(Ks + k_off[ks][0]),
+                           *(const lds_u32x4*)(Ks + k_off[ks][1]));
+      const u32x8 a1 = cat(*(const lds_u32x4*)(Ks + k_off[ks][0] + 32 * D),
+                           *(const lds_u32x4*)(Ks + k_off[ks][1] + 32 * D));
+      sacc[0] = mfma_fp8(a0, qT[ks], sacc[0]);
+      sacc[1] = mfma_fp8(a1, qT[ks], sacc[1]);
+    }
+  };
+  // The rest of tile t: mask, online softmax, P.V.
+  auto finish = [&](int t, int st, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+    const int j0 = t * kBc8;
+    {
+      const lds_char* Vs = lds + st * G::kStageBytes + G::kTileBytes;
 
       // V^T operands: read g (0..3) covers keys 32 (g/2) + 16 (g%2) + 8 hf + 0..7.
       const uint32_t vs_addr = (uint32_t)(uintptr_t)Vs;
@@ -316,7 +330,36 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
         acc[t2] = mfma_fp8(va, pb, acc[t2]);
       }
     }
+  };
+  // One tile from ring stage st.
+  auto tile = [&](int t, int st) __attribute__((always_inline)) {
+    if (!wave_idle(t)) {
+      f32x16 sacc[2];
+      scores(st, sacc);
+      finish(t, st, sacc);
+    }
+  };
 
+#if FA8_GROUP > 1
+  // kGroup8 tiles between barriers: they are computed from half of the ring
+  // while the next kGroup8 land in the other half.
+  for (int t = t_begin; t < t_end; t += kGroup8) {
+    const int it = t - t_begin;
+#pragma unroll
+    for (int g = 0; g < kGroup8; ++g)
+      if (t + kGroup8 + g < t_end) issue_tile(t + kGroup8 + g, (it + kGroup8 + g) % kRing8);
+#pragma unroll
+    for (int g = 0; g < kGroup8; ++g)
+      if (t + g < t_end) tile(t + g, (it + g) % kRing8);
+    wait_vm_lgkm0<0>();
+    bare_barrier();
+  }
+#else
+  for (int t = t_begin; t < t_end; ++t) {
+    const int it = t - t_begin;
+    const bool pre = t + kStages8 - 1 < t_end;
+    if (pre) issue_tile(t + kStages8 - 1, (it + kStages8 - 1) % kStages8);
+    tile(t, it % kStages8);
     // This wave's part of tile t+1 has landed and its reads of stage st are
     // done; after the barrier every wave may read t+1 and refill stage st.
     if (pre) {
@@ -326,6 +369,7 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     }
     bare_barrier();
   }
+#endif
 
   // -------- epilogue: O = acc * v_descale / l, zero for rows without keys --------
   if (qrow >= n) return;
