@@ -271,7 +271,8 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
 
 // One wave per (sequence, query head): merge the splits' (m, l, acc).  Lane s
 // reads split s's (m, l); the weights 2^(m_s - M) are shared across the wave
-// and every lane sums its D/64 columns over the splits.
+// and every lane sums its D/64 columns over the splits, eight splits' loads
+// in flight at a time.
 template <class T, int D>
 __global__ __launch_bounds__(64) void fa_decode_merge(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
@@ -299,11 +300,22 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
     const float wgt = s < ns ? fast_exp2(part_m[base + s] - M) : 0.f;
     if (s < ns) l = fmaf(wgt, part_l[base + s], l);
     const int cnt = min(64, ns - s0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __shfl(wgt, j);
-      const float* src = part_acc + (base + s0 + j) * D + lane * PER;
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float x[8][PER], wj[8];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) a[e] = fmaf(wj, src[e], a[e]);
+      for (int u = 0; u < 8; ++u) {
+        // Past cnt: re-read the last split (in bounds, written by this call)
+        // and give it weight 0.
+        const int j = min(j0 + u, cnt - 1);
+        wj[u] = j0 + u < cnt ? __shfl(wgt, j0 + u) : 0.f;
+        const float* src = part_acc + (base + s0 + j) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[u][e] = src[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a[e] = fmaf(wj[u], x[u][e], a[e]);
     }
   }
 #pragma unroll
