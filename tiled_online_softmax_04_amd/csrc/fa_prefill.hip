@@ -297,15 +297,28 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       f32x16 sacc[2][kNT];
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) sacc[0][nt] = sacc[1][nt] = f32x16{};
+      // K operands in batches of four k-steps: a batch's LDS reads are all
+      // issued before its MFMAs, so the MFMAs do not wait out one read's
+      // latency each (left to itself the compiler pairs every read with the
+      // MFMA that uses it).
+      constexpr int KB = G::kQSteps < 4 ? G::kQSteps : 4;
+      static_assert(G::kQSteps % KB == 0, "batch");
 #pragma unroll
-      for (int ks = 0; ks < G::kQSteps; ++ks) {
-        const u32x4 a0 = *(const lds_u32x4*)(Ks + k_off[ks]);
-        const u32x4 a1 = *(const lds_u32x4*)(Ks + k_off[ks] + 32 * D * 2);
+      for (int kb = 0; kb < G::kQSteps; kb += KB) {
+        u32x4 ka[KB][2];
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          sacc[0][nt] = T::mfma32x32x16(a0, qT[nt][ks], sacc[0][nt]);
-          sacc[1][nt] = T::mfma32x32x16(a1, qT[nt][ks], sacc[1][nt]);
+        for (int u = 0; u < KB; ++u) {
+          ka[u][0] = *(const lds_u32x4*)(Ks + k_off[kb + u]);
+          ka[u][1] = *(const lds_u32x4*)(Ks + k_off[kb + u] + 32 * D * 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) {
+            sacc[0][nt] = T::mfma32x32x16(ka[u][0], qT[nt][kb + u], sacc[0][nt]);
+            sacc[1][nt] = T::mfma32x32x16(ka[u][1], qT[nt][kb + u], sacc[1][nt]);
+          }
       }
 
       // V^T operands through transposing reads: 2 reads per (k-step j, dv tile).
