@@ -141,3 +141,34 @@ def test_fp8_full_size_sampled():
         ref, B_, sig = fp8_bound.row_bounds(q, rows, k, v, w.scale)
         got = to_f64(o[b, h, torch.from_numpy(rows).cuda()], "bf16")
         fp8_bound.check(got, ref, B_, sig, f"cfg2_fp8 b={b} h={h} rows={rows.tolist()}", say)
+
+
+def test_fp8_causal_8k_sampled_and_deterministic():
+    """The causal 8192-token shape (32 heads) stored as FP8: sampled rows from
+    the first, the last and the tile-boundary positions within the bound, the
+    first row equal to V's first row up to the output rounding, and two calls
+    bitwise equal."""
+    import dataclasses
+    import torch
+    w = dataclasses.replace(gen.WORKLOADS["cfg3"], dtype="fp8", name="cfg3_fp8")
+    say("[fp8] causal 8192 x 32 heads, sampled rows")
+    x = gen.make_prefill(w)
+    q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
+    args = (q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"])
+    o = fa.fwd_fp8(*args, scale=w.scale, causal=True)
+    o2 = fa.fwd_fp8(*args, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "not deterministic"
+    assert bool(torch.isfinite(o.float()).all())
+    rng = np.random.default_rng(17)
+    for h in (0, 13, w.Hq - 1):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 4095, w.n - 1],
+                                         rng.integers(0, w.n, size=8)]))
+        q = oracle.dequantize(x["q"][0, h, rows], x["q_descale"])
+        k = oracle.dequantize(x["k"][0, h], x["k_descale"])
+        v = oracle.dequantize(x["v"][0, h], x["v_descale"])
+        ref, B_, sig = fp8_bound.row_bounds(q, rows, k, v, w.scale, causal=True)
+        got = to_f64(o[0, h, torch.from_numpy(rows).cuda()], "bf16")
+        fp8_bound.check(got, ref, B_, sig, f"cfg3_fp8 h={h} rows={rows.tolist()}", say)
+        # row 0 attends key 0 only: O = V[0] up to the bf16 output
+        assert np.all(np.abs(got[0] - v[0]) <= 2.0 ** -8 * np.abs(v[0]))
