@@ -159,13 +159,13 @@ def test_decode_rejects_before_launch(lib, kw, code):
 
 def test_decode_workspace_size(lib):
     # 64 sequences x 32 query heads, up to 512 blocks of 16 keys: 512-key splits
-    # -> 16 splits, each holding (m, l, acc[128]) in float32
-    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * 130 * 4
+    # -> 16 splits, each holding m and l in float32 and o[128] in 16 bits
+    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * (8 + 256)
     assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 0, 16) == 0
     assert lib.fa_paged_decode_workspace_size(64, 32, 0, 128, 512, 16) == 0
     # a lone sequence gets smaller splits so the GPU still fills
     one = lib.fa_paged_decode_workspace_size(1, 32, 8, 128, 512, 16)
-    assert one > 32 * 16 * 130 * 4
+    assert one > 32 * 16 * (8 + 256)
 
 
 def test_binding_rejects_host_tensors():

