@@ -196,6 +196,28 @@ def test_decode_small(case):
             assert np.all(got[s] == 0)
 
 
+@pytest.mark.parametrize("dtype,factor", [("f16", 2.0e4), ("bf16", 1.0e30)])
+def test_decode_large_values(dtype, factor):
+    """Values near the top of the input type's range: each split's output is a
+    weighted mean of V rows, kept in the input type between the two passes, so
+    it must stay finite and as accurate, relative to max |V|, as at unit scale.
+    Several 512-key splits per sequence are merged."""
+    name = f"large_{dtype}"
+    say(f"[decode] {name}")
+    w = gen.Decode(name, dtype, 3, 8, 2, 128, 128, 16, 1, 1, 200, seed=31)
+    x = gen.make_decode(w, seq_lens=[3000, 1500, 700])
+    v = gen.to_f64(x["v_cache"], dtype) * factor  # NaN tail slots stay NaN
+    if dtype == "f16":
+        v = np.clip(v, -60000.0, 60000.0)
+    x["v_cache"] = gen.store(v.astype(np.float32), dtype)
+    vmax = float(np.nanmax(np.abs(gen.to_f64(x["v_cache"], dtype))))
+    scale = float(np.float32(1 / np.sqrt(128)))
+    got = to_f64(run_decode(x, dtype, 16, scale), dtype)
+    ref = decode_oracle(x, dtype, 16, scale)
+    assert np.isfinite(got).all()
+    assert_parity(got / vmax, ref / vmax, dtype, f"{name} (relative to max |V| = {vmax:.3g})")
+
+
 def test_decode_cfg4_full():
     w = gen.WORKLOADS["cfg4"]
     say("[decode] cfg4 generating")
