@@ -118,15 +118,18 @@ def test_merge_reproduces_full_pass(case):
             assert np.all(got[b, :, :p] == 0)
 
 
-def test_merge_kernel_on_oracle_pieces():
+@pytest.mark.parametrize("bounds", [[0, 17, 17, 40, 64], [0, 9, 17, 17, 30, 40, 64]],
+                         ids=["4pieces", "6pieces"])
+def test_merge_kernel_on_oracle_pieces(bounds):
     """The merge alone: pieces computed by the oracle (float32), merged on the
-    GPU, against the oracle's merge_lse; includes rows covered by no piece."""
+    GPU, against the oracle's merge_lse; includes rows covered by no piece.
+    The o of a piece without keys (lse = -inf) is never read: poisoning it
+    with NaN leaves the result bitwise unchanged."""
     import torch
     rng = np.random.default_rng(31)
     B, Hq, n, m, d = 2, 3, 50, 64, 64
     q, k, v = (rng.standard_normal(s) for s in [(B, Hq, n, d), (B, Hq, m, d), (B, Hq, m, d)])
     pads = [0, 20]
-    bounds = [0, 17, 17, 40, 64]
     parts = [oracle.attention_range(q, k, v, 0.125, True, pads, lo, hi)
              for lo, hi in zip(bounds[:-1], bounds[1:])]
     o32 = [p_[0].astype(np.float32) for p_ in parts]
@@ -143,6 +146,14 @@ def test_merge_kernel_on_oracle_pieces():
     out16 = fa.merge(o_parts, l_parts, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_parity(to_f64(out16, "bf16"), ref_o, "bf16", "merge of oracle pieces, bf16 out")
+    empty = torch.isinf(l_parts) & (l_parts < 0)
+    assert bool(empty.any())
+    poisoned = o_parts.clone()
+    poisoned[empty] = float("nan")
+    out_p, lse_p = fa.merge(poisoned, l_parts, out_dtype=torch.float32, want_lse=True)
+    out_c, lse_c = fa.merge(o_parts, l_parts, out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out_c) and torch.equal(lse_p, lse_c)
 
 
 def test_full_size_key_split_sampled():

@@ -11,7 +11,10 @@
 //
 // One thread per 4 adjacent columns of a row (16-byte loads of every piece);
 // a workgroup covers 256 / (dv / 4) consecutive rows.  The pass is bandwidth
-// bound (it reads every piece once) and runs on the vector ALUs.
+// bound (it reads every piece once) and runs on the vector ALUs.  The pieces
+// are read four at a time with all their loads in flight together, o with
+// nontemporal loads (read once); a piece without keys is left out by a
+// select, so its o never reaches the sum whatever it holds.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -19,6 +22,7 @@
 namespace fa {
 
 constexpr int kMergeThreads = 256;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 template <int OUT>  // output type: 0 float32, 1 float16, 2 bfloat16
 __global__ __launch_bounds__(kMergeThreads) void fa_merge_lse(
@@ -31,23 +35,39 @@ __global__ __launch_bounds__(kMergeThreads) void fa_merge_lse(
   if (row >= rows) return;
   const int c = (threadIdx.x - r_local * quads) * 4;
 
+  const float* lse_row = lse_parts + row;
+  const float* o_row = o_parts + (size_t)row * dv + c;
+  const size_t o_step = (size_t)rows * dv;
   float L = -__builtin_inff();
-  for (int s = 0; s < parts; ++s) L = fmaxf(L, lse_parts[(size_t)s * rows + row]);
+  for (int s = 0; s < parts; ++s) L = fmaxf(L, lse_row[(size_t)s * rows]);
   const bool has = L > -__builtin_inff();
   float W = 0.f;
   float4 a = {0.f, 0.f, 0.f, 0.f};
-  if (has) {
-    for (int s = 0; s < parts; ++s) {
-      const float ls = lse_parts[(size_t)s * rows + row];
-      if (!(ls > -__builtin_inff())) continue;  // a piece without keys weighs nothing
-      const float w = expf(ls - L);
+  constexpr int kBatch = 4;
+  for (int s0 = 0; s0 < parts; s0 += kBatch) {
+    float ls[kBatch];
+    f32x4 x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u < parts) {  // uniform across the grid
+        ls[u] = lse_row[(size_t)(s0 + u) * rows];
+        x[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(o_row + (size_t)(s0 + u) * o_step));
+      } else {
+        ls[u] = -__builtin_inff();
+        x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      // a piece without keys weighs nothing and its o is not used
+      const bool ok = has && ls[u] > -__builtin_inff();
+      const float w = ok ? expf(ls[u] - L) : 0.f;
       W += w;
-      const float4 x =
-          *reinterpret_cast<const float4*>(o_parts + ((size_t)s * rows + row) * dv + c);
-      a.x = fmaf(w, x.x, a.x);
-      a.y = fmaf(w, x.y, a.y);
-      a.z = fmaf(w, x.z, a.z);
-      a.w = fmaf(w, x.w, a.w);
+      a.x = ok ? fmaf(w, x[u][0], a.x) : a.x;
+      a.y = ok ? fmaf(w, x[u][1], a.y) : a.y;
+      a.z = ok ? fmaf(w, x[u][2], a.z) : a.z;
+      a.w = ok ? fmaf(w, x[u][3], a.w) : a.w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
