@@ -13,7 +13,8 @@ before timing starts.  Prints one JSON line:
   cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
 After the timed steps, the same prefill is also timed as four key-range pieces
 plus their merge, as a paged causal chunk over the decode cache, and with FP8
-(E4M3) inputs against the FP8 MFMA peak.
+(E4M3) inputs against the FP8 MFMA peak; and the causal prefill B=1 H=32
+n=m=8192 is timed beside its dense twin.
 """
 from __future__ import annotations
 
@@ -211,6 +212,42 @@ def time_fp8(fa, iters: int):
                                    "bf16 out)"}}
 
 
+def time_causal(fa, iters: int):
+    """The causal bf16 prefill B=1 H=32 n=m=8192 d=128, and the same inputs
+    without the mask (its dense twin); HIP events around each fa_fwd call.
+    The causal FLOPs count only unmasked pairs."""
+    import torch
+    from tiled_online_softmax_04_amd import inputs as gen
+    if iters <= 0:
+        return None
+    w = gen.WORKLOADS["cfg3"]
+    x = gen.make_prefill(w)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x[t]).view(np.int16)).cuda()
+               .view(torch.bfloat16) for t in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    res = {}
+    for causal in (True, False):
+        for _ in range(max(50, iters)):
+            fa.fwd(q, k, v, scale=w.scale, causal=causal, out=out)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        for e0, e1 in evs:
+            e0.record()
+            fa.fwd(q, k, v, scale=w.scale, causal=causal, out=out)
+            e1.record()
+        torch.cuda.synchronize()
+        res[causal] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    flop_causal = gen.prefill_flops(w)
+    flop_dense = 4.0 * w.B * w.Hq * w.n * w.m * w.d
+    return {"workload": "causal prefill bf16 B=1 H=32 n=m=8192 d=dv=128, and its dense twin "
+                        "(the same inputs without the mask)",
+            "tflops": round(flop_causal / (res[True] * 1e-3) / 1e12, 2),
+            "ms": round(res[True], 5),
+            "dense_twin_tflops": round(flop_dense / (res[False] * 1e-3) / 1e12, 2),
+            "dense_twin_ms": round(res[False], 5),
+            "time_ratio": round(res[True] / res[False], 4), "iters": iters}
+
+
 def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
     """Peak device memory of one attention head, beyond its inputs and output:
     the tiled library call against the plain three-step evaluation that keeps
@@ -263,6 +300,9 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 skips it)")
     ap.add_argument("--key-split-iters", type=int, default=30,
                     help="timed runs of the key-split, paged-prefill and FP8 variants after the "
+                         "step (0 skips them)")
+    ap.add_argument("--causal-iters", type=int, default=20,
+                    help="timed runs of the causal 8192 prefill and its dense twin after the "
                          "step (0 skips them)")
     ap.add_argument("--peak-memory", type=int, default=1,
                     help="1: also report peak device memory, tiled vs naive, at n = 512, 2048, "
@@ -345,6 +385,7 @@ def main():
     key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
     paged = time_paged_prefill(fa, wd, kc, vc, bt, sl, xd["seq_lens"], args.key_split_iters)
     fp8 = time_fp8(fa, args.key_split_iters)
+    causal = time_causal(fa, args.causal_iters)
     mem = peak_memory(fa) if args.peak_memory else None
 
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
@@ -388,6 +429,7 @@ def main():
         "key_split": key_split,
         "paged_prefill": paged,
         "fp8": fp8,
+        "causal": causal,
         "peak_memory": mem,
     }
     print(json.dumps(out), flush=True)
