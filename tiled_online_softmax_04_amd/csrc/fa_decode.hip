@@ -6,8 +6,9 @@
 // ("它如何与你已经搭好的部分组合").  Decode has a single query row, so the
 // parallelism comes from the keys instead (flash-decoding, S12): the key range
 // of a sequence is cut into splits, each split runs the online-softmax
-// recurrence in its own workgroup and leaves a partial (m, l, acc), and a second
-// kernel merges the partials with the same rescale (S12 exercise 1).
+// recurrence in its own workgroup and leaves a partial state (m, l, o = acc / l),
+// and a second kernel merges the partials with the same rescale (S12
+// exercise 1).
 //
 // This pass moves about 4 FLOP per byte, far below the MFMA ridge point, so it
 // is bandwidth bound: the kernel streams K/V with 16-byte loads straight into
