@@ -57,11 +57,6 @@ static_assert(kStages == 2 || kStages == 3, "ring depth");
 // 2 * kGroup stages: one half is computed while the next group lands in the
 // other half.  The paged form keeps one tile per barrier (its block table
 // shares LDS with the ring).
-// Q tiles per workgroup for the full non-causal call (see the launcher).
-#ifndef FA_PREFILL_MULTI
-#define FA_PREFILL_MULTI 1
-#endif
-constexpr int kCUs = 256;  // compute units of the MI355X
 #ifndef FA_PREFILL_GROUP
 #define FA_PREFILL_GROUP 2
 #endif
@@ -126,15 +121,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ Of,
     float* __restrict__ Lse, const int32_t* __restrict__ seq_lens, int Hq, int group, int n,
     int m, int key_begin, int key_end, int q_tiles, int total, float c,
-    const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks,
-    int per_wg) {
+    const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks) {
   using G = Geo<D>;
-  // Several Q tiles per workgroup (per_wg, chosen by the host) only where every
-  // Q tile of a head reads the same key tiles: the K/V ring then streams on
-  // from one Q tile into the next, and the next tile's first K/V DMA overlaps
-  // the current tile's last tiles and output.
-  constexpr bool kMulti = !CAUSAL && !RAGGED && !PARTIAL && !PAGED && kGroup > 1;
-  const int per = kMulti ? per_wg : 1;
   constexpr int kGrp = PAGED ? 1 : kGroup;
   constexpr int kRing = ring_stages(PAGED);
   extern __shared__ __align__(16) uint16_t smem[];
@@ -144,7 +132,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int ql = lane & 31, hf = lane >> 5;
 
-  const int logical = xcd_contiguous(blockIdx.x, total) * per;  // first Q-tile unit
+  const int logical = xcd_contiguous(blockIdx.x, total);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   // Causal tiles further down hold more keys: hand those out first.
@@ -165,21 +153,18 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   // Paged chunk: key position of query row i is qoff + i, qoff = L - n.
   const int L = PAGED ? __builtin_amdgcn_readfirstlane(min(max(seq_lens[b], 0), maxb * bs)) : 0;
   const int qoff = PAGED ? L - n : 0;
-  int wg_q0 = qt * kBr;
+  const int wg_q0 = qt * kBr;
   const int wg_q1 = min(n, wg_q0 + kBr);
-  int wq0 = wg_q0 + w * kQPerWave;  // first query of this wave
+  const int wq0 = wg_q0 + w * kQPerWave;  // first query of this wave
   int qrow[kNT];
   bool q_ok[kNT];
-  auto set_rows = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      qrow[nt] = wq0 + 32 * nt + ql;
-      // Rows that hold no real query: past n, inside the left pad, or (paged)
-      // before the first token of the sequence.
-      q_ok[nt] = qrow[nt] < n && (PAGED ? qrow[nt] + qoff >= 0 : qrow[nt] >= pad);
-    }
-  };
-  set_rows();
+  for (int nt = 0; nt < kNT; ++nt) {
+    qrow[nt] = wq0 + 32 * nt + ql;
+    // Rows that hold no real query: past n, inside the left pad, or (paged)
+    // before the first token of the sequence.
+    q_ok[nt] = qrow[nt] < n && (PAGED ? qrow[nt] + qoff >= 0 : qrow[nt] >= pad);
+  }
 
   // Keys this call may attend: [key_lo, key_hi) -- past the left pad and
   // inside the requested range (the whole of [0, m) for a full call).
@@ -262,28 +247,22 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
   // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive d.
   u32x4 qT[kNT][G::kQSteps];
-  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
+  for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < G::kQSteps; ++ks)
-        qT[nt][ks] = q_ok[nt] ? load16(Qh + (size_t)qrow[nt] * D + ks * 16 + hf * 8)
-                              : u32x4{0, 0, 0, 0};
-  };
-  load_q();
+    for (int ks = 0; ks < G::kQSteps; ++ks)
+      qT[nt][ks] = q_ok[nt] ? load16(Qh + (size_t)qrow[nt] * D + ks * 16 + hf * 8)
+                            : u32x4{0, 0, 0, 0};
 
   f32x16 acc[G::kOTiles][kNT];
   float m_run[kNT], l_run[kNT];
-  auto init_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
 #pragma unroll
-      for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] = f32x16{};
-      m_run[nt] = kSentinel;  // running max (scaled log2 units)
-      l_run[nt] = 0.f;        // this lane's half of the running sum
-    }
-  };
-  init_state();
+    for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] = f32x16{};
+    m_run[nt] = kSentinel;  // running max (scaled log2 units)
+    l_run[nt] = 0.f;        // this lane's half of the running sum
+  }
 
   // Per-lane LDS byte offsets of the MFMA operands within a stage.
   uint32_t k_off[G::kQSteps];  // K rows ql (and +32) for each k-step
@@ -452,18 +431,48 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     }
   };
 
-  // O = acc / l for the rows given, zero for rows without keys.
-  auto store_out = [&](const int (&rows)[kNT], const bool (&ok)[kNT])
-      __attribute__((always_inline)) {
+  if constexpr (kGrp > 1) {
+    // kGrp tiles from one half of the ring while the next kGrp land in the
+    // other half; one barrier per group.
+    for (int t = t_begin; t < t_end; t += kGrp) {
+      const int it = t - t_begin;
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g)
+        if (t + kGrp + g < t_end) issue_tile(t + kGrp + g, (it + kGrp + g) % kRing);
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g)
+        if (t + g < t_end) tile(t + g, (it + g) % kRing);
+      wait_vm_lgkm0<0>();
+      bare_barrier();
+    }
+  } else {
+    for (int t = t_begin; t < t_end; ++t) {
+      const int it = t - t_begin;
+      // Refill the stage read in the previous iteration with tile t+kStages-1.
+      const bool pre = t + kStages - 1 < t_end;
+      if (pre) issue_tile(t + kStages - 1, (it + kStages - 1) % kStages);
+      tile(t, it % kStages);
+      // This wave's part of tile t+1 has landed and its reads of stage st are
+      // done; after the barrier every wave may read t+1 and refill stage st.
+      if (kStages == 3 && pre) {
+        wait_vm_lgkm0<(kStages - 2) * G::kDmaPerWave>();  // tile t+2 may stay in flight
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      bare_barrier();
+    }
+  }
+
+  // -------- epilogue: O = acc / l, zero for rows without keys --------
+  if constexpr (PARTIAL) {
+    // float32 O of the range and lse = ln(2^m * l) (m is in log2 units).
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const float l_tot = sum_xor32(l_run[nt]);
-      const bool has = l_tot > 0.f && ok[nt];
+      const bool has = l_tot > 0.f && q_ok[nt];
       const float inv = has ? 1.f / l_tot : 0.f;
-      if (rows[nt] >= n) continue;
-      if constexpr (PARTIAL) {
-        // float32 O of the range and lse = ln(2^m * l) (m is in log2 units).
-        float* orow = Of + q_base + (size_t)rows[nt] * D;
+      if (qrow[nt] < n) {
+        float* orow = Of + q_base + (size_t)qrow[nt] * D;
 #pragma unroll
         for (int t2 = 0; t2 < G::kOTiles; ++t2) {
 #pragma unroll
@@ -478,83 +487,28 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
           }
         }
         if (hf == 0)
-          Lse[q_base / D + rows[nt]] =
+          Lse[q_base / D + qrow[nt]] =
               has ? (m_run[nt] + log2f(l_tot)) * kLn2 : -__builtin_inff();
-      } else {
-        uint16_t* orow = O + q_base + (size_t)rows[nt] * D;
-#pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int dv0 = 32 * t2 + 8 * g + 4 * hf;
-            const uint32_t lo = T::pack(acc[t2][nt][4 * g] * inv, acc[t2][nt][4 * g + 1] * inv);
-            const uint32_t hi =
-                T::pack(acc[t2][nt][4 * g + 2] * inv, acc[t2][nt][4 * g + 3] * inv);
-            *reinterpret_cast<u32x2*>(orow + dv0) = u32x2{lo, hi};
-          }
-        }
       }
     }
-  };
-
-  const int n_tiles = t_end - t_begin;
-  int run = 0;  // ring position of the current Q tile's first key tile
-  for (int qi = 0; qi < per; ++qi) {
-    if (qi > 0) wait_vm_lgkm0<0>();  // this Q tile's queries have landed
-    if constexpr (kGrp > 1) {
-      // kGrp tiles from one half of the ring while the next kGrp land in the
-      // other half; one barrier per group.
-      for (int t = t_begin; t < t_end; t += kGrp) {
-        const int it = run + t - t_begin;  // ring position of tile t
+    return;
+  }
 #pragma unroll
-        for (int g = 0; g < kGrp; ++g) {
-          const int nx = t + kGrp + g;
-          if (nx < t_end)
-            issue_tile(nx, (it + kGrp + g) % kRing);
-          else if (kMulti && qi + 1 < per && nx - n_tiles < t_end)
-            issue_tile(nx - n_tiles, (it + kGrp + g) % kRing);  // the next Q tile's first tiles
+  for (int nt = 0; nt < kNT; ++nt) {
+    const float l_tot = sum_xor32(l_run[nt]);
+    const float inv = (l_tot > 0.f && q_ok[nt]) ? 1.f / l_tot : 0.f;
+    if (qrow[nt] < n) {
+      uint16_t* orow = O + q_base + (size_t)qrow[nt] * D;
+#pragma unroll
+      for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dv0 = 32 * t2 + 8 * g + 4 * hf;
+          const uint32_t lo = T::pack(acc[t2][nt][4 * g] * inv, acc[t2][nt][4 * g + 1] * inv);
+          const uint32_t hi = T::pack(acc[t2][nt][4 * g + 2] * inv, acc[t2][nt][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + dv0) = u32x2{lo, hi};
         }
-#pragma unroll
-        for (int g = 0; g < kGrp; ++g)
-          if (t + g < t_end) tile(t + g, (it + g) % kRing);
-        wait_vm_lgkm0<0>();
-        bare_barrier();
       }
-    } else {
-      for (int t = t_begin; t < t_end; ++t) {
-        const int it = t - t_begin;
-        // Refill the stage read in the previous iteration with tile t+kStages-1.
-        const bool pre = t + kStages - 1 < t_end;
-        if (pre) issue_tile(t + kStages - 1, (it + kStages - 1) % kStages);
-        tile(t, it % kStages);
-        // This wave's part of tile t+1 has landed and its reads of stage st are
-        // done; after the barrier every wave may read t+1 and refill stage st.
-        if (kStages == 3 && pre) {
-          wait_vm_lgkm0<(kStages - 2) * G::kDmaPerWave>();  // tile t+2 may stay in flight
-        } else {
-          wait_vm_lgkm0<0>();
-        }
-        bare_barrier();
-      }
-    }
-    run += n_tiles;
-    if (qi + 1 < per) {
-      // The next Q tile's queries go out before this one's output.
-      int rows_now[kNT];
-      bool ok_now[kNT];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        rows_now[nt] = qrow[nt];
-        ok_now[nt] = q_ok[nt];
-      }
-      wg_q0 += kBr;
-      wq0 += kBr;
-      set_rows();
-      load_q();
-      store_out(rows_now, ok_now);
-      init_state();
-    } else {
-      store_out(qrow, q_ok);
     }
   }
 }
@@ -686,22 +640,12 @@ static hipError_t launch_mfma(const FwdArgs& a) {
   if (attr != hipSuccess) return attr;
   const int bs = PG ? a.block_size : 1;
   const int shift = (PG && (bs & (bs - 1)) == 0) ? __builtin_ctz((unsigned)bs) : -1;
-  // The full non-causal call takes several Q tiles of a head per workgroup:
-  // as many as still leave one workgroup for each of the 256 CUs.
-  int per = 1;
-  if (FA_PREFILL_MULTI && !C && !R && !P && !PG && kGroup > 1)
-    for (int pq = 4; pq > 1; pq /= 2)
-      if (q_tiles % pq == 0 && total / pq >= kCUs) {
-        per = pq;
-        break;
-      }
-  const long long wgs = total / per;
-  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P, PG>), dim3((unsigned)wgs), dim3(kThreads), lds,
+  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P, PG>), dim3((unsigned)total), dim3(kThreads), lds,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.o_f32, a.lse, a.seq_lens,
                      a.heads_q, a.heads_q / a.heads_kv, a.n, a.m, a.key_begin, a.key_end,
-                     q_tiles, (int)wgs, a.scale * kLog2e, a.block_table, bs, shift,
-                     a.max_blocks, a.num_blocks, per);
+                     q_tiles, (int)total, a.scale * kLog2e, a.block_table, bs, shift,
+                     a.max_blocks, a.num_blocks);
   return hipGetLastError();
 }
 
