@@ -71,6 +71,34 @@ def test_prefill_small(case):
                     assert np.array_equal(got[b, h, p], v[b, h // (Hq // Hkv), p])
 
 
+WIDE = [
+    # name, dtype, B, Hq, Hkv, n, m, d: many heads, key-tile counts odd or with a
+    # ragged tail
+    ("wide_bf16_d64_gqa_odd_tiles", "bf16", 2, 64, 16, 1024, 1025, 64),
+    ("wide_f16_d128_ragged_tail", "f16", 2, 64, 64, 1024, 1000, 128),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
+def test_prefill_many_heads_ragged_keys(case):
+    """Non-causal calls of 512 workgroups whose key ranges end inside a tile
+    (17 tiles at m = 1025, 16 at m = 1000): every output row of sampled heads
+    against the oracle, and the whole output finite."""
+    name, dtype, B, Hq, Hkv, n, m, d = case
+    say(f"[prefill] {name}")
+    x = gen.make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, d,
+                                seed=zlib.crc32(name.encode()) % 1000)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    got = to_f64(run_prefill(x, dtype, False, scale, None), dtype)
+    assert np.isfinite(got).all()
+    q, k, v = f64_inputs(x, dtype)
+    g = Hq // Hkv
+    for b, h in [(0, 0), (0, 1), (1, Hq // 2 + 1), (1, Hq - 1)]:
+        ref = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1],
+                               v[b:b + 1, h // g:h // g + 1], scale, False)
+        assert_parity(got[b:b + 1, h:h + 1], ref, dtype, f"{name} b={b} h={h}")
+
+
 @pytest.mark.parametrize("name", ["cfg1", "cfg1_hot"])
 def test_cfg1_fp32(name):
     w = gen.WORKLOADS[name]
