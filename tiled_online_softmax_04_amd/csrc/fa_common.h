@@ -149,6 +149,19 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int total) {
   return base + k;
 }
 
+// Logical id of workgroup bid over total units laid out as groups of
+// per_group consecutive units (a KV group: its query heads' Q tiles).  When
+// the groups come in multiples of 8, XCD x takes groups x, x + 8, ... with
+// each group's units back to back: units that share a group's K/V meet in
+// one L2, and every XCD gets groups from every sequence of a ragged or paged
+// batch (contiguous ranges would give each XCD a few whole sequences, and the
+// longest would set the time).  Otherwise each XCD takes one contiguous range.
+__device__ __forceinline__ int xcd_by_group(int bid, int total, int per_group) {
+  if ((total / per_group) % 8 != 0) return xcd_contiguous(bid, total);
+  const int x = bid % 8, k = bid / 8;
+  return (x + 8 * (k / per_group)) * per_group + k % per_group;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {

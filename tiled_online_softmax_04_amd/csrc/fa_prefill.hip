@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int ql = lane & 31, hf = lane >> 5;
 
-  const int logical = xcd_contiguous(blockIdx.x, total);
+  // Work units are (batch, query head, Q tile), Q tiles fastest; the units of
+  // one KV group (batch, KV head) are consecutive.
+  const int logical = xcd_by_group(blockIdx.x, total, group * q_tiles);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   // Causal tiles further down hold more keys: hand those out first.

@@ -133,7 +133,9 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ql = lane & 31, hf = lane >> 5;
 
-  const int logical = xcd_contiguous(blockIdx.x, total);
+  // Units (batch, query head, Q tile), Q tiles fastest; KV groups dealt to
+  // the XCDs in turn.
+  const int logical = xcd_by_group(blockIdx.x, total, group * q_tiles);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   const int qt = CAUSAL ? q_tiles - 1 - qt_ord : qt_ord;  // longest causal rows first
