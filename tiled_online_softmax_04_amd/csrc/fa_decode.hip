@@ -287,6 +287,8 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
   }
 }
 
+constexpr int kMergeFast = 16;  // splits the merge reads in one go
+
 // One wave per (sequence, query head): merge the splits' (m, l, o).  Lane s
 // reads split s's (m, l); the weights 2^(m_s - M) l_s are shared across the
 // wave and every lane sums its D/64 columns of the o_s over the splits, eight
@@ -302,6 +304,60 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
   const int L = seq_lens[seq];
   const int ns = min(max((L + split_tokens - 1) / split_tokens, 0), max_splits);
   const size_t base = ((size_t)seq * Hq + h) * max_splits;
+
+  uint16_t* orow = O + ((size_t)seq * Hq + h) * D + lane * PER;
+  auto store = [&](const float (&a)[PER], float inv) {
+    if constexpr (PER == 2) {
+      *reinterpret_cast<uint32_t*>(orow) = T::pack(a[0] * inv, a[1] * inv);
+    } else {
+      const uint32_t x = T::pack(a[0] * inv, 0.f);
+      orow[0] = (uint16_t)(x & 0xffffu);
+    }
+  };
+  if (ns <= kMergeFast) {
+    // Up to kMergeFast splits (every sequence of up to 8192 keys at 512-key
+    // splits): all loads go out at once -- (m, l) of split `lane` and this
+    // lane's columns of every split's o -- so the pass waits out one memory
+    // latency instead of three.  Splits at or past ns re-read split ns - 1
+    // (in bounds, written by this call) and weigh 0.
+    float a[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) a[e] = 0.f;
+    if (ns == 0) {  // no keys: O = 0
+      store(a, 0.f);
+      return;
+    }
+    const bool mine = lane < ns;
+    const float ms = mine ? part_m[base + lane] : -__builtin_inff();
+    const float lsv = mine ? part_l[base + lane] : 0.f;
+    float x[kMergeFast][PER];
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const uint16_t* src = part_o + (base + min(u, ns - 1)) * D + lane * PER;
+      if constexpr (PER == 2) {
+        const uint32_t pr = *reinterpret_cast<const uint32_t*>(src);
+        x[u][0] = T::lo(pr);
+        x[u][1] = T::hi(pr);
+      } else {
+        x[u][0] = T::lo((uint32_t)src[0]);
+      }
+    }
+    float M = ms;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float wgt = mine ? fast_exp2(ms - M) * lsv : 0.f;
+    float l = wgt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+#pragma unroll
+    for (int u = 0; u < kMergeFast; ++u) {
+      const float wu = __shfl(wgt, u);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) a[e] = fmaf(wu, x[u][e], a[e]);
+    }
+    store(a, l > 0.f ? 1.f / l : 0.f);
+    return;
+  }
 
   // pass 1: the largest running max over all splits
   float M = -__builtin_inff();
@@ -343,14 +399,7 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint16_t* orow = O + ((size_t)seq * Hq + h) * D + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(orow) = T::pack(a[0] * inv, a[1] * inv);
-  } else {
-    const uint32_t x = T::pack(a[0] * inv, 0.f);
-    orow[0] = (uint16_t)(x & 0xffffu);
-  }
+  store(a, l > 0.f ? 1.f / l : 0.f);
 }
 
 // ---------------------------------------------------------------------------
