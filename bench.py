@@ -13,8 +13,9 @@ before timing starts.  Prints one JSON line:
   cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
 After the timed steps, the same prefill is also timed as four key-range pieces
 plus their merge, as a paged causal chunk over the decode cache, and with FP8
-(E4M3) inputs against the FP8 MFMA peak; and the causal prefill B=1 H=32
-n=m=8192 is timed beside its dense twin.
+(E4M3) inputs against the FP8 MFMA peak; the causal prefill B=1 H=32
+n=m=8192 is timed beside its dense twin, and the hot fp16 causal prefill
+B=1 H=16 n=m=16384 with its count of non-finite outputs.
 """
 from __future__ import annotations
 
@@ -239,13 +240,35 @@ def time_causal(fa, iters: int):
         res[causal] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     flop_causal = gen.prefill_flops(w)
     flop_dense = 4.0 * w.B * w.Hq * w.n * w.m * w.d
+    del q, k, v, out
+    # the hot long-context case: fp16, Q and K x10 (scores far past the fp16
+    # exp overflow point); the whole output must be finite
+    w5 = gen.WORKLOADS["cfg5"]
+    x5 = gen.make_prefill(w5)
+    q5, k5, v5 = (torch.from_numpy(np.ascontiguousarray(x5[t])).cuda() for t in ("q", "k", "v"))
+    out5 = torch.empty_like(q5)
+    for _ in range(max(20, iters)):
+        fa.fwd(q5, k5, v5, scale=w5.scale, causal=True, out=out5)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record()
+        fa.fwd(q5, k5, v5, scale=w5.scale, causal=True, out=out5)
+        e1.record()
+    torch.cuda.synchronize()
+    ms5 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    nonfinite5 = int((~torch.isfinite(out5)).sum().item())
     return {"workload": "causal prefill bf16 B=1 H=32 n=m=8192 d=dv=128, and its dense twin "
                         "(the same inputs without the mask)",
             "tflops": round(flop_causal / (res[True] * 1e-3) / 1e12, 2),
             "ms": round(res[True], 5),
             "dense_twin_tflops": round(flop_dense / (res[False] * 1e-3) / 1e12, 2),
             "dense_twin_ms": round(res[False], 5),
-            "time_ratio": round(res[True] / res[False], 4), "iters": iters}
+            "time_ratio": round(res[True] / res[False], 4), "iters": iters,
+            "hot_fp16_16384": {"workload": "causal prefill fp16 B=1 H=16 n=m=16384 d=dv=128, Q and "
+                                           "K drawn x10 (scores up to ~300)",
+                               "tflops": round(gen.prefill_flops(w5) / (ms5 * 1e-3) / 1e12, 2),
+                               "ms": round(ms5, 5), "nonfinite_outputs": nonfinite5}}
 
 
 def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
