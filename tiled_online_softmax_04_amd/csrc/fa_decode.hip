@@ -46,7 +46,7 @@
 
 namespace fa {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;  // per split: 8 chunks of 16 tokens each in flight
 constexpr int kDecThreads = 64 * kDecWaves;
 #ifndef FA_DECODE_CHUNK
 #define FA_DECODE_CHUNK 16
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
     }
   };
 
-  // The 4 waves take the 16-token chunks of the split in turn.
+  // The waves take the 16-token chunks of the split in turn.
   constexpr int kStep = kDecWaves * kDecChunk;
   __syncthreads();  // block-table entries staged in LDS
   for (int t0 = tok0 + w * kDecChunk; t0 < tok1; t0 += kStep) {
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
   }
   __syncthreads();
 
-  // Merge the 4 waves' states; one thread per (head, pair of columns).  The
+  // Merge the waves' states; one thread per (head, pair of columns).  The
   // split's output o = acc / l goes out as 16-bit pairs; l >= 1 for a split
   // that holds keys (its largest key has weight exp2(0) = 1).
   for (int x = tid; x < GW * D / 2; x += kDecThreads) {
