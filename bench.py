@@ -7,15 +7,23 @@ workload the headline metric is quoted on) followed by one paged GQA decode call
 [512, 8192]).  Inputs are seeded synthetic tensors resident in device memory
 before timing starts.  Prints one JSON line:
 
-  value     prefill TFLOP/s (algorithmic: 4*d FLOP per (query, key) pair)
+  value     prefill TFLOP/s (algorithmic: 4*d FLOP per (query, key) pair), mean
+            over the timed steps (median and min beside it)
   roofline  the prefill kernel against the bf16 dense MFMA peak
   decode    paged decode GB/s (algorithmic bytes) against HBM peak
-  cpu_baseline  the float64 oracle on a bounded sample, on this host's cores
-After the timed steps, the same prefill is also timed as four key-range pieces
-plus their merge, as a paged causal chunk over the decode cache, and with FP8
-(E4M3) inputs against the FP8 MFMA peak; the causal prefill B=1 H=32
-n=m=8192 is timed beside its dense twin, and the hot fp16 causal prefill
-B=1 H=16 n=m=16384 with its count of non-finite outputs.
+  cpu_baseline  the float64 oracle on a bounded sample of every workload, on
+            this host's cores
+
+Order of the run: first the process's first steps are timed call by call
+(`cold_start`, a fresh GPU ramps its clock over them); then the other
+workloads, each with its own roofline object: the left-padded ragged causal
+batch B=8 x 8192, the causal prefill B=1 H=32 n=m=8192 beside its dense twin,
+the hot fp16 causal prefill B=1 H=16 n=m=16384 with its count of non-finite
+outputs, the headline prefill as four key-range pieces plus their merge, as a
+paged causal chunk over the decode cache and with FP8 (E4M3) inputs, and peak
+device memory tiled vs naive.  Then the warmup steps and the timed steps, so
+the timed steps run at the clock a busy GPU holds.  The oracle runs last, on
+the CPU only.
 """
 from __future__ import annotations
 
@@ -44,6 +52,7 @@ FP8_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_prefill_fp8.hip",
                "tiled_online_softmax_04_amd/csrc/fa_common.h"]
 DECODE_SOURCES = ["tiled_online_softmax_04_amd/csrc/fa_decode.hip",
                   "tiled_online_softmax_04_amd/csrc/fa_common.h"]
+PREFILL_KERNEL = "fa_fwd_mfma<BF16,128,{c},{r},false,{p}>"
 
 
 def source_digest(paths) -> str:
@@ -74,39 +83,107 @@ def read_traffic(name: str, paths):
         return None
 
 
-def cpu_baseline(w, x, budget_s: float):
-    """Time the float64 oracle on whole (batch, head) slices of the workload until
-    about `budget_s` seconds of CPU work, and scale to TFLOP/s."""
-    import oracle
-    from tiled_online_softmax_04_amd import inputs as gen
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    done, t_used, flops = 0, 0.0, 0.0
-    per_head = 4.0 * w.n * w.m * w.d
-    for b, h in heads:
-        q = gen.to_f64(x["q"][b:b + 1, h:h + 1], w.dtype)
-        k = gen.to_f64(x["k"][b:b + 1, h:h + 1], w.dtype)
-        v = gen.to_f64(x["v"][b:b + 1, h:h + 1], w.dtype)
-        t0 = time.perf_counter()
-        oracle.attention(q, k, v, w.scale, w.causal)
-        t_used += time.perf_counter() - t0
-        done += 1
-        flops += per_head
-        if t_used >= budget_s:
-            break
-    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s",
-            "cores": int(min(threads, len(os.sched_getaffinity(0)))), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (batch, head) slices of the same workload, "
-                      f"float64, {t_used:.1f} s"}
+def stats(ms) -> dict:
+    """Mean, median and min of per-call times (ms)."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean_ms": round(float(a.mean()), 5), "median_ms": round(float(np.median(a)), 5),
+            "min_ms": round(float(a.min()), 5), "calls": int(a.size)}
 
 
-def time_key_split(fa, q, k, v, wp, iters: int):
-    """The same prefill as four 512-key pieces (fa_fwd_partial) merged by
-    fa_merge; timed outside the step, after it, with HIP events."""
+def roofline(achieved: float, peak: float, unit: str, bound: str, traffic, kernel: str) -> dict:
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+
+
+def timed_calls(run, iters: int, warm: int):
+    """`warm` untimed calls, then `iters` calls each bracketed by HIP events on
+    torch's current stream (the stream the library launches on); per-call ms."""
+    import torch
+    for _ in range(warm):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def to_dev(a, dtype, dev):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+# --------------------------------------------------------------------------
+# GPU legs outside the timed step
+# --------------------------------------------------------------------------
+def cold_start(step, n: int):
+    """The first `n` steps of the process, each call timed on its own: a fresh
+    GPU ramps its clock over them."""
+    import torch
+    if n <= 0:
+        return None
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    return {"prefill_ms": [round(e[0].elapsed_time(e[1]), 4) for e in evs],
+            "decode_ms": [round(e[1].elapsed_time(e[2]), 4) for e in evs]}
+
+
+def prefill_leg(fa, gen, name: str, x, iters: int, warm: int, dev, label: str):
+    """One full-size prefill workload (inputs `x` drawn beforehand): HIP events
+    around each fa.fwd call, FLOPs of its unmasked pairs (the drawn lengths for
+    a ragged batch)."""
+    import torch
+    w = gen.WORKLOADS[name]
+    q, k, v = (to_dev(x[t], w.dtype, dev) for t in ("q", "k", "v"))
+    sl = None if x["seq_lens"] is None else torch.from_numpy(x["seq_lens"]).to(dev)
+    out = torch.empty_like(q)
+    ms = timed_calls(lambda: fa.fwd(q, k, v, scale=w.scale, causal=w.causal, seq_lens=sl,
+                                    out=out), iters, warm)
+    flops = gen.prefill_flops(w, x["seq_lens"])
+    st = stats(ms)
+    tflops = flops / (st["mean_ms"] * 1e-3) / 1e12
+    res = {"workload": label, "flop": flops, "tflops": round(tflops, 2), **st,
+           "tflops_at_median": round(flops / (st["median_ms"] * 1e-3) / 1e12, 2),
+           "nonfinite_outputs": int((~torch.isfinite(out.float())).sum().item()),
+           "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
+                                PREFILL_KERNEL.format(c=str(w.causal).lower(),
+                                                      r=str(x["seq_lens"] is not None).lower(),
+                                                      p="false").replace("BF16", w.dtype.upper()))}
+    if x["seq_lens"] is not None:
+        res["seq_lens"] = [int(a) for a in x["seq_lens"]]
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_dense_twin(fa, gen, w, x, iters, warm, dev):
+    """The causal 8192 inputs without the mask: the time ratio shows the
+    skipped tiles."""
+    import torch
+    q, k, v = (to_dev(x[t], w.dtype, dev) for t in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    ms = timed_calls(lambda: fa.fwd(q, k, v, scale=w.scale, causal=False, out=out), iters, warm)
+    st = stats(ms)
+    flops = 4.0 * w.B * w.Hq * w.n * w.m * w.d
+    tflops = flops / (st["mean_ms"] * 1e-3) / 1e12
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return {"tflops": round(tflops, 2), **st,
+            "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
+                                 PREFILL_KERNEL.format(c="false", r="false", p="false"))}
+
+
+def time_key_split(fa, gen, q, k, v, wp, iters: int):
+    """The headline prefill as four 512-key pieces (fa_fwd_partial) merged by
+    fa_merge, with HIP events around the pieces and around the merge."""
     import torch
     if iters <= 0:
         return None
@@ -133,148 +210,76 @@ def time_key_split(fa, q, k, v, wp, iters: int):
     for e in evs:
         run(e)
     torch.cuda.synchronize()
-    part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    merge_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    part = stats([e[0].elapsed_time(e[1]) for e in evs])
+    merge = stats([e[1].elapsed_time(e[2]) for e in evs])
     rows = B * Hq * n
     merge_bytes = 4 * rows * (dv + 1) * 4 + rows * dv * 2
-    from tiled_online_softmax_04_amd import inputs as gen
     flops = gen.prefill_flops(wp)
-    return {"workload": "the prefill above as keys [0,512) [512,1024) [1024,1536) [1536,2048) "
-                        "through fa_fwd_partial, then fa_merge",
-            "tflops_total": round(flops / ((part_ms + merge_ms) * 1e-3) / 1e12, 2),
-            "tflops_pieces": round(flops / (part_ms * 1e-3) / 1e12, 2),
-            "pieces_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5),
-            "merge_gbps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
-            "merge_bytes": merge_bytes, "iters": iters}
+    pieces_tflops = flops / (part["mean_ms"] * 1e-3) / 1e12
+    merge_gbps = merge_bytes / (merge["mean_ms"] * 1e-3) / 1e9
+    return {"workload": "the headline prefill as keys [0,512) [512,1024) [1024,1536) "
+                        "[1536,2048) through fa_fwd_partial, then fa_merge",
+            "tflops_total": round(flops / ((part["mean_ms"] + merge["mean_ms"]) * 1e-3) / 1e12, 2),
+            "pieces": {**part, "tflops": round(pieces_tflops, 2),
+                       "roofline": roofline(pieces_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
+                                            None, "fa_fwd_mfma<BF16,128,false,false,true,false>")},
+            "merge": {**merge, "gbps": round(merge_gbps, 1), "bytes": merge_bytes,
+                      "roofline": roofline(merge_gbps, PEAK_HBM_GBPS, "GB/s", "hbm", None,
+                                           "fa_merge_lse<2>")}}
 
 
-def time_paged_prefill(fa, wd, kc, vc, bt, sl, seq_lens, iters: int, n: int = 512):
+def time_paged_prefill(fa, gen, wd, kc, vc, bt, sl, seq_lens, iters: int, n: int = 512):
     """A 512-token causal chunk per sequence over the decode workload's paged
-    cache (the chunk being the last 512 tokens of each sequence); HIP events
-    around fa_paged_prefill, after the step."""
+    cache (the chunk being the last 512 tokens of each sequence)."""
     import torch
-    from tiled_online_softmax_04_amd import inputs as gen
     if iters <= 0:
         return None
     g = torch.Generator(device="cpu").manual_seed(wd.seed + 1)
     q = torch.randn((wd.num_seqs, wd.Hq, n, wd.d), generator=g).to(torch.bfloat16).to(kc.device)
     out = torch.empty((wd.num_seqs, wd.Hq, n, wd.dv), dtype=q.dtype, device=q.device)
-    for _ in range(max(10, iters // 2)):
-        fa.paged_prefill(q, kc, vc, bt, sl, wd.block_size, scale=wd.scale, out=out)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        fa.paged_prefill(q, kc, vc, bt, sl, wd.block_size, scale=wd.scale, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    ms = timed_calls(lambda: fa.paged_prefill(q, kc, vc, bt, sl, wd.block_size, scale=wd.scale,
+                                              out=out), iters, max(10, iters // 2))
+    st = stats(ms)
     flops = gen.paged_prefill_flops(seq_lens, n, wd.Hq, wd.d, wd.dv, causal=True)
+    tflops = flops / (st["mean_ms"] * 1e-3) / 1e12
     return {"workload": f"paged prefill bf16: a {n}-token causal chunk at the end of each of the "
                         "decode workload's 64 sequences (Hq=32, Hkv=8, d=128, 16-token blocks, "
                         "random placement)",
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 5), "flop": flops,
-            "iters": iters}
+            "tflops": round(tflops, 2), "flop": flops, **st,
+            "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
+                                 "fa_fwd_mfma<BF16,128,true,false,false,true>")}
 
 
-def time_fp8(fa, iters: int):
+def time_fp8(fa, gen, x, iters: int):
     """The headline prefill with Q, K, V stored as FP8 E4M3 (per-tensor
-    descales) and a bf16 output; HIP events around each fa_fwd_fp8 call."""
+    descales) and a bf16 output; `x` holds the drawn codes."""
     import torch
-    from tiled_online_softmax_04_amd import inputs as gen
     if iters <= 0:
         return None
     w = gen.WORKLOADS["cfg2_fp8"]
-    x = gen.make_prefill(w)
     q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
     out = torch.empty((w.B, w.Hq, w.n, w.dv), dtype=torch.bfloat16, device=q8.device)
-
-    def run():
-        fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"], scale=w.scale,
-                   out=out)
-
-    for _ in range(max(200, iters)):   # steady clocks after the other legs
-        run()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for e0, e1 in evs:
-        e0.record()
-        run()
-        e1.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    tflops = gen.prefill_flops(w) / (ms * 1e-3) / 1e12
-    return {"workload": "the prefill above (B=4 H=32 n=m=2048 d=dv=128 non-causal) with Q, K, V "
-                        "stored as FP8 E4M3 with per-tensor descales, bf16 output",
-            "tflops": round(tflops, 2), "ms": round(ms, 5), "iters": iters,
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4),
-                         "traffic": read_traffic("fa_fwd_fp8_cfg2_traffic.txt", FP8_SOURCES),
-                         "kernel": "fa_fwd_fp8<128,false,false,2> (non-causal, no padding, "
-                                   "bf16 out)"}}
-
-
-def time_causal(fa, iters: int):
-    """The causal bf16 prefill B=1 H=32 n=m=8192 d=128, and the same inputs
-    without the mask (its dense twin); HIP events around each fa_fwd call.
-    The causal FLOPs count only unmasked pairs."""
-    import torch
-    from tiled_online_softmax_04_amd import inputs as gen
-    if iters <= 0:
-        return None
-    w = gen.WORKLOADS["cfg3"]
-    x = gen.make_prefill(w)
-    q, k, v = (torch.from_numpy(np.ascontiguousarray(x[t]).view(np.int16)).cuda()
-               .view(torch.bfloat16) for t in ("q", "k", "v"))
-    out = torch.empty_like(q)
-    res = {}
-    for causal in (True, False):
-        for _ in range(max(50, iters)):
-            fa.fwd(q, k, v, scale=w.scale, causal=causal, out=out)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(iters)]
-        for e0, e1 in evs:
-            e0.record()
-            fa.fwd(q, k, v, scale=w.scale, causal=causal, out=out)
-            e1.record()
-        torch.cuda.synchronize()
-        res[causal] = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    flop_causal = gen.prefill_flops(w)
-    flop_dense = 4.0 * w.B * w.Hq * w.n * w.m * w.d
-    del q, k, v, out
-    # the hot long-context case: fp16, Q and K x10 (scores far past the fp16
-    # exp overflow point); the whole output must be finite
-    w5 = gen.WORKLOADS["cfg5"]
-    x5 = gen.make_prefill(w5)
-    q5, k5, v5 = (torch.from_numpy(np.ascontiguousarray(x5[t])).cuda() for t in ("q", "k", "v"))
-    out5 = torch.empty_like(q5)
-    for _ in range(max(20, iters)):
-        fa.fwd(q5, k5, v5, scale=w5.scale, causal=True, out=out5)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
-    for e0, e1 in evs:
-        e0.record()
-        fa.fwd(q5, k5, v5, scale=w5.scale, causal=True, out=out5)
-        e1.record()
-    torch.cuda.synchronize()
-    ms5 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    nonfinite5 = int((~torch.isfinite(out5)).sum().item())
-    return {"workload": "causal prefill bf16 B=1 H=32 n=m=8192 d=dv=128, and its dense twin "
-                        "(the same inputs without the mask)",
-            "tflops": round(flop_causal / (res[True] * 1e-3) / 1e12, 2),
-            "ms": round(res[True], 5),
-            "dense_twin_tflops": round(flop_dense / (res[False] * 1e-3) / 1e12, 2),
-            "dense_twin_ms": round(res[False], 5),
-            "time_ratio": round(res[True] / res[False], 4), "iters": iters,
-            "hot_fp16_16384": {"workload": "causal prefill fp16 B=1 H=16 n=m=16384 d=dv=128, Q and "
-                                           "K drawn x10 (scores up to ~300)",
-                               "tflops": round(gen.prefill_flops(w5) / (ms5 * 1e-3) / 1e12, 2),
-                               "ms": round(ms5, 5), "nonfinite_outputs": nonfinite5}}
+    ms = timed_calls(lambda: fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"],
+                                        x["v_descale"], scale=w.scale, out=out),
+                     iters, max(50, iters))
+    st = stats(ms)
+    tflops = gen.prefill_flops(w) / (st["mean_ms"] * 1e-3) / 1e12
+    return {"workload": "the headline prefill (B=4 H=32 n=m=2048 d=dv=128 non-causal) with Q, K, "
+                        "V stored as FP8 E4M3 with per-tensor descales, bf16 output",
+            "tflops": round(tflops, 2), **st,
+            "roofline": roofline(tflops, PEAK_FP8_TFLOPS, "TFLOP/s", "mfma",
+                                 read_traffic("fa_fwd_fp8_cfg2_traffic.txt", FP8_SOURCES),
+                                 "fa_fwd_fp8<128,false,false,2> (non-causal, no padding, "
+                                 "bf16 out)")}
 
 
 def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
-    """Peak device memory of one attention head, beyond its inputs and output:
-    the tiled library call against the plain three-step evaluation that keeps
-    S and P (float32) in device memory (exercise 3 of the S12 chapter)."""
+    """Device memory of one attention head beyond its inputs and output: the
+    tiled library call against the plain three-step evaluation that keeps S and
+    P (float32) in device memory (exercise 3 of the S12 chapter).  Two views:
+    torch's allocator peak, and the device's free memory (hipMemGetInfo) before
+    the call, right after it is enqueued and after it has finished, which would
+    also see memory the library took for itself."""
     import torch
     dev = torch.device("cuda:0")
     out = []
@@ -284,11 +289,15 @@ def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
                    for _ in range(3))
         o = torch.empty_like(q)
         scale = 1.0 / math.sqrt(d)
+        fa.fwd(q, k, v, scale=scale, out=o)   # first call: code objects loaded
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated(dev)
         torch.cuda.reset_peak_memory_stats(dev)
+        free0 = torch.cuda.mem_get_info(dev)[0]
         fa.fwd(q, k, v, scale=scale, out=o)
+        free1 = torch.cuda.mem_get_info(dev)[0]
         torch.cuda.synchronize()
+        free2 = torch.cuda.mem_get_info(dev)[0]
         flash_extra = torch.cuda.max_memory_allocated(dev) - base
         kt = k.float()[0, 0].t().contiguous()
 
@@ -305,6 +314,7 @@ def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
         torch.cuda.synchronize()
         naive_extra = torch.cuda.max_memory_allocated(dev) - base2
         out.append({"n": n, "flash_extra_bytes": int(flash_extra),
+                    "flash_device_free_drop_bytes": int(free0 - min(free1, free2)),
                     "naive_extra_bytes": int(naive_extra),
                     "n2_float32_bytes": 4 * n * n})
         del o2, kt, q, k, v, o
@@ -312,21 +322,106 @@ def peak_memory(fa, sizes=(512, 2048, 8192), d=128):
     return out
 
 
+# --------------------------------------------------------------------------
+# the oracle on the host cores
+# --------------------------------------------------------------------------
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def oracle_prefill_sample(w, x, budget_s: float, rows: int = 512):
+    """The oracle (as it stands) on blocks of `rows` query rows of successive
+    (batch, head) slices until about `budget_s` seconds; TFLOP/s of the
+    unmasked pairs of the rows it computed."""
+    import oracle
+    from tiled_online_softmax_04_amd import inputs as gen
+    g = w.Hq // w.Hkv
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    used, flops, blocks = 0.0, 0.0, 0
+    rng = np.random.default_rng(7)
+    while used < budget_s:
+        b, h = heads[blocks % len(heads)]
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        k = gen.to_f64(x["k"][b, h // g], w.dtype)
+        v = gen.to_f64(x["v"][b, h // g], w.dtype)
+        r0 = pad + int(rng.integers(0, max(1, w.n - pad - rows + 1)))
+        r1 = min(w.n, r0 + rows)
+        q = gen.to_f64(x["q"][b, h, r0:r1], w.dtype)
+        t0 = time.perf_counter()
+        oracle.attend(q, np.arange(r0, r1), k, v, w.scale, w.causal, pad)
+        used += time.perf_counter() - t0
+        idx = np.arange(r0, r1)
+        keys = (idx - pad + 1) if w.causal else np.full(idx.size, w.m - pad)
+        flops += float(keys.sum()) * (2 * w.d + 2 * w.dv)
+        blocks += 1
+    return {"value": round(flops / used / 1e12, 6), "unit": "TFLOP/s", "seconds": round(used, 2),
+            "sample": f"{blocks} blocks of up to {rows} consecutive query rows at random offsets, "
+                      f"(batch, head) slices in turn, all keys of each row, float64"}
+
+
+def oracle_decode_sample(w, x, budget_s: float):
+    """The oracle's paged decode on successive sequences until about
+    `budget_s` seconds; GB/s of those sequences' algorithmic bytes."""
+    import oracle
+    from tiled_online_softmax_04_amd import inputs as gen
+    q = gen.to_f64(x["q"], w.dtype)
+    kc = gen.to_f64(x["k_cache"], w.dtype)
+    vc = gen.to_f64(x["v_cache"], w.dtype)
+    used, done = 0.0, 0
+    for s in range(w.num_seqs):
+        if used >= budget_s:
+            break
+        t0 = time.perf_counter()
+        oracle.paged_decode(q[s:s + 1], kc, vc, x["block_table"][s:s + 1], x["seq_lens"][s:s + 1],
+                            w.block_size, w.scale)
+        used += time.perf_counter() - t0
+        done += 1
+    L = np.asarray(x["seq_lens"][:done], dtype=np.int64)
+    e = gen.ELEM_BYTES[w.dtype]
+    nbytes = (int(L.sum()) * w.Hkv * (w.d + w.dv) * e + done * w.Hq * (w.d + w.dv) * e
+              + int(((L + w.block_size - 1) // w.block_size).sum()) * 4 + 4 * done)
+    return {"value": round(nbytes / used / 1e9, 4), "unit": "GB/s", "seconds": round(used, 2),
+            "sample": f"{done} of {w.num_seqs} sequences, float64"}
+
+
+def cpu_baselines(gen, budget_s: float, drawn: dict):
+    """The oracle timed on the host cores on a bounded sample of every
+    workload; the headline's figure is the `cpu_baseline` of the line.
+    `drawn` holds the drawn inputs of every workload."""
+    W = gen.WORKLOADS
+    per = {}
+    share = budget_s / 6.0
+    head = oracle_prefill_sample(W["cfg2"], drawn["cfg2"], 2 * share)
+    per["cfg2"] = head
+    for name in ("cfg1", "cfg1_hot"):
+        per[name] = oracle_prefill_sample(W[name], gen.make_prefill(W[name]), 0.5 * share,
+                                          rows=256)
+    for name in ("cfg3", "cfg3_ragged", "cfg5"):
+        per[name] = oracle_prefill_sample(W[name], drawn[name], share)
+    per["cfg4"] = oracle_decode_sample(W["cfg4"], drawn["cfg4"], share)
+    return {"value": head["value"], "unit": "TFLOP/s", "cores": int(min(blas_threads(),
+                                                                        len(os.sched_getaffinity(0)))),
+            "kind": "oracle", "sample": "headline workload: " + head["sample"],
+            "numpy": np.__version__, "host_cores": len(os.sched_getaffinity(0)),
+            "configs": per}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the GPU needs a few hundred calls to "
-                         "reach steady clocks")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle work for the CPU baseline (0 skips it)")
-    ap.add_argument("--key-split-iters", type=int, default=30,
-                    help="timed runs of the key-split, paged-prefill and FP8 variants after the "
-                         "step (0 skips them)")
-    ap.add_argument("--causal-iters", type=int, default=20,
-                    help="timed runs of the causal 8192 prefill and its dense twin after the "
-                         "step (0 skips them)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-budget", type=float, default=24.0,
+                    help="seconds of oracle work for the CPU baselines of all workloads "
+                         "(0 skips them)")
+    ap.add_argument("--cold-steps", type=int, default=25,
+                    help="the process's first steps, timed call by call (0 skips them)")
+    ap.add_argument("--leg-iters", type=int, default=30,
+                    help="timed calls of each workload outside the step (0 skips those legs)")
     ap.add_argument("--peak-memory", type=int, default=1,
                     help="1: also report peak device memory, tiled vs naive, at n = 512, 2048, "
                          "8192 (0 skips it)")
@@ -346,21 +441,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    def to_dev(a, dtype):
-        a = np.ascontiguousarray(a)
-        if dtype == "bf16":
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+    # every input is drawn before the first GPU call, so that no host work
+    # leaves the GPU idle between the legs and the timed steps
+    it = args.leg_iters
+    drawn = {"cfg2": gen.make_prefill(gen.WORKLOADS["cfg2"]),
+             "cfg4": gen.make_decode(gen.WORKLOADS["cfg4"])}
+    if it > 0 or args.cpu_budget > 0:
+        for name in ("cfg3_ragged", "cfg3", "cfg5"):
+            drawn[name] = gen.make_prefill(gen.WORKLOADS[name])
+    if it > 0:
+        drawn["cfg2_fp8"] = gen.make_prefill(gen.WORKLOADS["cfg2_fp8"])
 
     wp = gen.WORKLOADS["cfg2"]
-    xp = gen.make_prefill(wp)
-    q, k, v = (to_dev(xp[n], wp.dtype) for n in ("q", "k", "v"))
+    xp = drawn["cfg2"]
+    q, k, v = (to_dev(xp[n], wp.dtype, dev) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
 
     wd = gen.WORKLOADS["cfg4"]
-    xd = gen.make_decode(wd)
-    dq = to_dev(xd["q"], wd.dtype)
-    kc, vc = to_dev(xd["k_cache"], wd.dtype), to_dev(xd["v_cache"], wd.dtype)
+    xd = drawn["cfg4"]
+    dq = to_dev(xd["q"], wd.dtype, dev)
+    kc, vc = to_dev(xd["k_cache"], wd.dtype, dev), to_dev(xd["v_cache"], wd.dtype, dev)
     bt = torch.from_numpy(xd["block_table"]).to(dev)
     sl = torch.from_numpy(xd["seq_lens"]).to(dev)
     do = torch.empty((wd.num_seqs, wd.Hq, wd.dv), dtype=dq.dtype, device=dev)
@@ -386,10 +486,35 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    flops = gen.prefill_flops(wp)
+    dbytes = gen.decode_bytes(wd, xd["seq_lens"])
+    cold = cold_start(step, args.cold_steps)
+
+    legs = {}
+    mem = peak_memory(fa) if args.peak_memory else None
+    if it > 0:
+        legs["ragged"] = prefill_leg(
+            fa, gen, "cfg3_ragged", drawn["cfg3_ragged"], max(10, it // 2), 10, dev,
+            "causal prefill bf16, left-padded ragged batch B=8 H=32 N=8192 d=dv=128, lengths "
+            "U[1024, 8192] (seed 3)")
+        causal = prefill_leg(fa, gen, "cfg3", drawn["cfg3"], it, 20, dev,
+                             "causal prefill bf16 B=1 H=32 n=m=8192 d=dv=128")
+        causal["dense_twin"] = time_dense_twin(fa, gen, gen.WORKLOADS["cfg3"], drawn["cfg3"], it,
+                                               10, dev)
+        causal["time_ratio"] = round(causal["mean_ms"] / causal["dense_twin"]["mean_ms"], 4)
+        legs["causal"] = causal
+        legs["hot_fp16_16384"] = prefill_leg(
+            fa, gen, "cfg5", drawn["cfg5"], it, 10, dev,
+            "causal prefill fp16 B=1 H=16 n=m=16384 d=dv=128, Q and K drawn x10 (scores up to "
+            "~300)")
+        legs["paged_prefill"] = time_paged_prefill(fa, gen, wd, kc, vc, bt, sl, xd["seq_lens"], it)
+        legs["fp8"] = time_fp8(fa, gen, drawn["cfg2_fp8"], it)
+        legs["key_split"] = time_key_split(fa, gen, q, k, v, wp, it)
+
+    # the headline: warmup steps, then exactly `steps` timed steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -398,25 +523,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    flops = gen.prefill_flops(wp)
-    dbytes = gen.decode_bytes(wd, xd["seq_lens"])
-    pre_tflops = flops / (pre_ms.mean() * 1e-3) / 1e12
-    dec_gbps = dbytes / (dec_ms.mean() * 1e-3) / 1e9
-
-    key_split = time_key_split(fa, q, k, v, wp, args.key_split_iters)
-    paged = time_paged_prefill(fa, wd, kc, vc, bt, sl, xd["seq_lens"], args.key_split_iters)
-    fp8 = time_fp8(fa, args.key_split_iters)
-    causal = time_causal(fa, args.causal_iters)
-    mem = peak_memory(fa) if args.peak_memory else None
+    pre = stats([e[0].elapsed_time(e[1]) for e in events])
+    dec = stats([e[1].elapsed_time(e[2]) for e in events])
+    pre_tflops = flops / (pre["mean_ms"] * 1e-3) / 1e12
+    dec_gbps = dbytes / (dec["mean_ms"] * 1e-3) / 1e9
 
     traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
     dec_traffic = read_traffic("fa_decode_cfg4_traffic.txt", DECODE_SOURCES)
 
-    baseline = None
-    if args.cpu_budget > 0:
-        baseline = cpu_baseline(wp, xp, args.cpu_budget)
+    baseline = cpu_baselines(gen, args.cpu_budget, drawn) if args.cpu_budget > 0 else None
 
     out = {
         "metric": "attn fwd TFLOP/s + % bf16 MFMA peak; paged decode GB/s + % HBM peak",
@@ -436,24 +551,21 @@ def main():
                                "lengths U[512,8192]",
                    "prefill_flop": flops, "decode_bytes": dbytes, "seed_prefill": wp.seed,
                    "seed_decode": wd.seed},
-        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "fa_fwd_mfma<BF16,128,false,false,false,false> (non-causal, no padding, full key range, contiguous)",
-                     "avg_launch_ms": round(float(pre_ms.mean()), 5)},
-        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
-                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1),
-                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                                "traffic": dec_traffic,
-                                "kernels": "fa_decode_split + fa_decode_merge",
-                                "avg_call_ms": round(float(dec_ms.mean()), 5)}},
+        "roofline": {**roofline(pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", traffic,
+                                "fa_fwd_mfma<BF16,128,false,false,false,false> (non-causal, no "
+                                "padding, full key range, contiguous)"),
+                     "avg_launch_ms": pre["mean_ms"]},
+        "prefill_times": {**pre, "tflops_at_median": round(flops / (pre["median_ms"] * 1e-3)
+                                                           / 1e12, 2)},
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s", **dec,
+                   "gbps_at_median": round(dbytes / (dec["median_ms"] * 1e-3) / 1e9, 1),
+                   "roofline": {**roofline(dec_gbps, PEAK_HBM_GBPS, "GB/s", "hbm", dec_traffic,
+                                           "fa_decode_split + fa_decode_merge"),
+                                "avg_call_ms": dec["mean_ms"]}},
         "cpu_baseline": baseline,
-        "key_split": key_split,
-        "paged_prefill": paged,
-        "fp8": fp8,
-        "causal": causal,
+        **legs,
         "peak_memory": mem,
+        "cold_start": cold,
     }
     print(json.dumps(out), flush=True)
 

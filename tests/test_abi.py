@@ -47,6 +47,22 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
+def test_library_imports_no_allocation_or_sync(lib):
+    """The library allocates and frees no device or host memory and never
+    synchronises (include/fa.h): its dynamic symbol table imports no HIP
+    allocation, free or synchronisation routine.  This is what makes the
+    tiled call's zero extra device memory hold by construction."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    imported = [line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()]
+    hip = [s for s in imported if s.startswith("hip")]
+    assert "hipLaunchKernel" in hip
+    banned = re.compile(r"^hip(Ext)?(Malloc|Free|HostMalloc|HostAlloc|HostFree|MemAlloc|"
+                        r"MallocManaged|MallocAsync|FreeAsync|MemPool|"
+                        r"DeviceSynchronize|StreamSynchronize|EventSynchronize|Memcpy)")
+    assert [s for s in hip if banned.match(s)] == []
+
+
 def test_status_strings(lib):
     for code, word in [(0, "ok"), (1, "invalid"), (2, "unsupported"), (3, "workspace"), (4, "HIP")]:
         assert word in lib.fa_status_string(code).decode()
@@ -159,13 +175,13 @@ def test_decode_rejects_before_launch(lib, kw, code):
 
 def test_decode_workspace_size(lib):
     # 64 sequences x 32 query heads, up to 512 blocks of 16 keys: 512-key splits
-    # -> 16 splits, each holding m and l in float32 and o[128] in 16 bits
-    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * (8 + 256)
+    # -> 16 splits, each holding m, l and o[128] in float32
+    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * (8 + 512)
     assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 0, 16) == 0
     assert lib.fa_paged_decode_workspace_size(64, 32, 0, 128, 512, 16) == 0
     # a lone sequence gets smaller splits so the GPU still fills
     one = lib.fa_paged_decode_workspace_size(1, 32, 8, 128, 512, 16)
-    assert one > 32 * 16 * (8 + 256)
+    assert one > 32 * 16 * (8 + 512)
 
 
 def test_binding_rejects_host_tensors():
@@ -173,6 +189,14 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x)
+    q3 = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    cache = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16)
+    table = torch.zeros(2, 2, dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa.paged_decode(q3, cache, cache, table, lens, 16)
+    with pytest.raises(ValueError):
+        fa.paged_prefill(q3[:, :, None], cache, cache, table, lens, 16)
 
 
 def partial(lib, dt=2, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, n=128, m=128, d=128, dv=128,

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on the
-same seeded inputs.  Small shapes are compared element by element; the full
-workload sizes are checked on sampled outputs and on properties that hold at
-any size (no inf/NaN, padding rows exactly 0, causal first row equal to V's)."""
+same seeded inputs, element by element: small shapes with ragged tails and
+edge cases, and every output of the full workload sizes, plus properties that
+hold at any size (no inf/NaN, padding rows exactly 0, causal first row equal
+to V's)."""
 import zlib
 
 import numpy as np
@@ -130,52 +131,79 @@ def test_prefill_deterministic():
 
 
 # --------------------------------------------------------------------------
-# full workload sizes: sampled outputs + whole-tensor properties
+# full workload sizes: every output element against the oracle
 # --------------------------------------------------------------------------
-def samples_for(w, pads, rng, count=40):
-    out = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.n - 1), (0, w.Hq // 2, 127), (0, 1, 128),
-           (w.B - 1, 0, w.n // 2)]
-    if pads is not None:
-        for b, p in enumerate(pads):
-            out += [(b, b % w.Hq, int(min(p, w.n - 1))), (b, (b + 1) % w.Hq, int(max(p - 1, 0)))]
-    while len(out) < count:
-        out.append((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.n))))
-    return out
+def host_workers() -> int:
+    """Worker threads for the oracle: this process's cores, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def whole_output_errors(x, w, got_bits):
+    """Max abs error, sum of abs errors and non-finite count of every output
+    element of a full-size prefill workload against the oracle.  The oracle
+    runs one (batch, head) at a time (its own row chunking bounds the memory),
+    the heads spread over a thread pool with single-threaded BLAS; ``got_bits``
+    is the device output copied to the host in its storage format."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    g = w.Hq // w.Hkv
+
+    def one(bh):
+        b, h = bh
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        q = gen.to_f64(x["q"][b, h], w.dtype)[None, None]
+        k = gen.to_f64(x["k"][b, h // g], w.dtype)[None, None]
+        v = gen.to_f64(x["v"][b, h // g], w.dtype)[None, None]
+        ref = oracle.attention(q, k, v, w.scale, w.causal, pads=[pad])[0, 0]
+        got = gen.to_f64(got_bits[b, h], w.dtype)
+        bad = int((~np.isfinite(got)).sum())
+        diff = np.abs(np.where(np.isfinite(got), got, 0.0) - ref)
+        return float(diff.max()), float(diff.sum()), bad
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(host_workers()) as pool:
+            res = list(pool.map(one, heads))
+    return (max(r[0] for r in res), sum(r[1] for r in res), sum(r[2] for r in res))
 
 
 @pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_ragged", "cfg5"])
-def test_full_size_sampled(name):
+def test_full_size_whole_output(name):
+    """The full workloads (bf16 2048 x 128 heads; causal 8192; the left-padded
+    ragged causal batch 8 x 8192; fp16 hot causal 16384) in the launch the
+    benchmark times: every output element against the oracle, at the bar
+    (max abs <= 1e-2, mean abs over the whole output <= 1e-3, no inf/NaN),
+    plus padding rows exactly 0 and the causal first row bitwise V's."""
+    import time
     import torch
     w = gen.WORKLOADS[name]
     say(f"[prefill] {name} generating")
     x = gen.make_prefill(w)
     say(f"[prefill] {name} running")
     o = run_prefill(x, w.dtype, w.causal, w.scale, x["pads"])
-    assert bool(torch.isfinite(o.float()).all()), "non-finite outputs"
     if x["pads"] is not None:
         for b, p in enumerate(x["pads"]):
-            assert bool((o[b, :, :int(p)] == 0).all())
-    say(f"[prefill] {name} oracle on samples")
-    rng = np.random.default_rng(100 + w.seed)
-    samples = samples_for(w, x["pads"], rng)
-    qs = gen.to_f64(x["q"], w.dtype) if w.B * w.n <= 8192 else None
-    # upcast only the heads the samples touch (the ragged batch is large)
-    got = np.stack([to_f64(o[b, h, i], w.dtype) for b, h, i in samples])
-    ref = np.zeros_like(got)
-    for t, (b, h, i) in enumerate(samples):
-        pad = 0 if x["pads"] is None else int(x["pads"][b])
-        if i < pad:
-            continue
-        qrow = gen.to_f64(x["q"][b, h, i], w.dtype)[None] if qs is None else qs[b, h, i][None]
-        kk = gen.to_f64(x["k"][b, h // (w.Hq // w.Hkv)], w.dtype)
-        vv = gen.to_f64(x["v"][b, h // (w.Hq // w.Hkv)], w.dtype)
-        ref[t] = oracle.attend(qrow, [i], kk, vv, w.scale, w.causal, pad)[0]
-    assert_parity(got, ref, w.dtype, f"{name} ({len(samples)} sampled rows)")
+            assert bool((o[b, :, :int(p)] == 0).all()), "padding rows must be exactly 0"
     if w.causal:
         p0 = 0 if x["pads"] is None else int(x["pads"][0])
         if p0 < w.n:
             row = to_f64(o[0, 0, p0], w.dtype)
             assert np.array_equal(row, gen.to_f64(x["v"][0, 0, p0], w.dtype))
+    if w.dtype == "bf16":
+        got_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got_bits = o.cpu().numpy()
+    del o
+    say(f"[prefill] {name} oracle on all {w.B * w.Hq} heads ({host_workers()} threads)")
+    t0 = time.perf_counter()
+    mx, total, bad = whole_output_errors(x, w, got_bits)
+    mean = total / got_bits.size
+    say(f"  {name} (all {got_bits.size} outputs, oracle {time.perf_counter() - t0:.1f} s): "
+        f"max_abs={mx:.3e} mean_abs={mean:.3e} nonfinite={bad}")
+    assert bad == 0, f"{bad} non-finite outputs"
+    assert mx <= 1e-2, f"max abs {mx:.3e} > 1e-2"
+    assert mean <= 1e-3, f"mean abs {mean:.3e} > 1e-3"
 
 
 # --------------------------------------------------------------------------
@@ -227,9 +255,10 @@ def test_decode_small(case):
 @pytest.mark.parametrize("dtype,factor", [("f16", 2.0e4), ("bf16", 1.0e30)])
 def test_decode_large_values(dtype, factor):
     """Values near the top of the input type's range: each split's output is a
-    weighted mean of V rows, kept in the input type between the two passes, so
-    it must stay finite and as accurate, relative to max |V|, as at unit scale.
-    Several 512-key splits per sequence are merged."""
+    weighted mean of V rows, handed from the split pass to the merge in fp32,
+    and the merged output must stay finite and as accurate, relative to
+    max |V|, as at unit scale.  Several 512-key splits per sequence are
+    merged."""
     name = f"large_{dtype}"
     say(f"[decode] {name}")
     w = gen.Decode(name, dtype, 3, 8, 2, 128, 128, 16, 1, 1, 200, seed=31)
@@ -244,6 +273,35 @@ def test_decode_large_values(dtype, factor):
     ref = decode_oracle(x, dtype, 16, scale)
     assert np.isfinite(got).all()
     assert_parity(got / vmax, ref / vmax, dtype, f"{name} (relative to max |V| = {vmax:.3g})")
+
+
+@pytest.mark.parametrize("dtype,offset", [("bf16", 3.0), ("f16", 20.0)])
+def test_decode_offset_values_absolute_bar(dtype, offset):
+    """V = offset + N(0,1), so every output sits where one ulp of the output
+    type is 2^-6 (bf16 in [2, 4), f16 in [16, 32)).  One correct rounding
+    errs by at most 2^-7 = 7.8e-3, inside the absolute 1e-2 bar; rounding each
+    split's output to 16 bits before the merge and again after it can reach
+    1.5e-2.  64 sequences of 600-1500 keys make 2-3 splits of 512 keys each.
+    The mean bar is 1e-3 above the mean error of the oracle's own output
+    rounded to the output type (about 3.9e-3 here, which no 16-bit output can
+    beat)."""
+    name = f"offset_{dtype}"
+    say(f"[decode] {name}")
+    w = gen.Decode(name, dtype, 64, 32, 8, 128, 128, 16, 600, 1500, 100, seed=41)
+    x = gen.make_decode(w)
+    v = gen.to_f64(x["v_cache"], dtype) + offset   # NaN tail slots stay NaN
+    x["v_cache"] = gen.store(v.astype(np.float32), dtype)
+    scale = float(np.float32(1 / np.sqrt(128)))
+    got = to_f64(run_decode(x, dtype, 16, scale), dtype)
+    ref = decode_oracle(x, dtype, 16, scale)
+    floor = float(np.abs(gen.to_f64(gen.store(ref.astype(np.float32), dtype), dtype) - ref).mean())
+    from gpu_util import metrics
+    mx, mean, bad = metrics(got, ref)
+    say(f"  {name}: max_abs={mx:.3e} mean_abs={mean:.3e} (rounding floor {floor:.3e}) "
+        f"nonfinite={bad}")
+    assert bad == 0
+    assert mx <= 1e-2, f"max abs {mx:.3e} > 1e-2"
+    assert mean <= floor + 1e-3, f"mean abs {mean:.3e} > {floor:.3e} + 1e-3"
 
 
 def test_decode_cfg4_full():
@@ -278,3 +336,39 @@ def test_decode_block_placement_invariance_and_determinism():
     y["block_table"] = t
     c = run_decode(y, "bf16", 16, w.scale)
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_binding_checks_caller_buffers():
+    """Caller-supplied out and workspace tensors are checked before the call:
+    host memory, the wrong shape or dtype, or a non-contiguous workspace raise
+    ValueError instead of reaching a kernel."""
+    import torch
+    say("[binding] caller buffers")
+    w = gen.Decode("buffers", "bf16", 2, 8, 2, 128, 128, 16, 1, 1, 8, seed=3)
+    x = gen.make_decode(w, seq_lens=[40, 100])
+    q = to_dev(x["q"], "bf16")
+    kc, vc = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+    bt = torch.from_numpy(x["block_table"]).cuda()
+    sl = torch.from_numpy(x["seq_lens"]).cuda()
+    good = torch.empty((2, 8, 128), dtype=torch.bfloat16, device="cuda")
+    bad_outs = [good.cpu(), good[:, :4], good.to(torch.float16),
+                torch.empty((2, 8, 256), dtype=torch.bfloat16, device="cuda")[:, :, :128]]
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            fa.paged_decode(q, kc, vc, bt, sl, 16, out=out)
+    need = fa.paged_decode_workspace_size(2, 8, 2, 128, 8, 16)
+    for ws in [torch.empty(need, dtype=torch.uint8), torch.empty(need // 2, dtype=torch.uint8,
+                                                                 device="cuda"),
+               torch.empty(2 * need, dtype=torch.uint8, device="cuda")[::2]]:
+        with pytest.raises(ValueError):
+            fa.paged_decode(q, kc, vc, bt, sl, 16, out=good, workspace=ws)
+    qc = q[:, :, None].contiguous()
+    for out in [good[:, :, None].cpu(), torch.empty((2, 8, 2, 128), dtype=torch.bfloat16,
+                                                     device="cuda")]:
+        with pytest.raises(ValueError):
+            fa.paged_prefill(qc, kc, vc, bt, sl, 16, out=out)
+    # the same calls with good buffers go through
+    fa.paged_decode(q, kc, vc, bt, sl, 16, out=good,
+                    workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    fa.paged_prefill(qc, kc, vc, bt, sl, 16, out=good[:, :, None].contiguous())
+    torch.cuda.synchronize()

@@ -35,11 +35,11 @@
 //  - K/V rows are read once per call, so their loads are marked nontemporal:
 //    the stream then does not push the partial states, written while it runs,
 //    out of the caches (measured: 10% faster than plain loads);
-//  - a split's partial output is stored as o = acc / l in the input's 16-bit
-//    type, beside fp32 m and l.  It is a weighted mean of V rows, so it lies in
-//    V's range and cannot overflow that type, and writes in the middle of the
-//    K/V read stream cost far more than their bytes suggest: halving them
-//    gained 4%.
+//  - a split's partial state is stored as fp32 m, l and o = acc / l, so the
+//    output is rounded to the 16-bit type once, in the merge.  (Rounding o to
+//    16 bits here as well would add a second rounding of the same size as the
+//    final one: for outputs in [2, 4) in bf16 the two together can exceed
+//    1e-2.)
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ seq_lens, int bs, int bs_shift, int Hq, int Hkv, int group, int subgroups,
     int maxb, int num_blocks, int split_tokens, int max_splits, float c,
-    float* __restrict__ part_m, float* __restrict__ part_l, uint16_t* __restrict__ part_o) {
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o) {
   using G = DecGeo<D>;
   constexpr int TPL = G::kTpl;
   __shared__ int bt_s[kMaxSplitBlocks];
@@ -255,25 +255,24 @@ __global__ __launch_bounds__(kDecThreads, FA_DECODE_WAVES_PER_EU) void fa_decode
   }
   __syncthreads();
 
-  // Merge the waves' states; one thread per (head, pair of columns).  The
-  // split's output o = acc / l goes out as 16-bit pairs; l >= 1 for a split
-  // that holds keys (its largest key has weight exp2(0) = 1).
-  for (int x = tid; x < GW * D / 2; x += kDecThreads) {
-    const int g = x / (D / 2), col = 2 * (x % (D / 2));
+  // Merge the waves' states; one thread per (head, column).  The split's
+  // output o = acc / l goes out in fp32; l >= 1 for a split that holds keys
+  // (its largest key has weight exp2(0) = 1).
+  for (int x = tid; x < GW * D; x += kDecThreads) {
+    const int g = x / D, col = x % D;
     float M = red_m[0][g];
 #pragma unroll
     for (int ww = 1; ww < kDecWaves; ++ww) M = fmaxf(M, red_m[ww][g]);
-    float l = 0.f, a0 = 0.f, a1 = 0.f;
+    float l = 0.f, a = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kDecWaves; ++ww) {
       const float f = fast_exp2(red_m[ww][g] - M);
       l = fmaf(f, red_l[ww][g], l);
-      a0 = fmaf(f, red_acc[ww][g][col], a0);
-      a1 = fmaf(f, red_acc[ww][g][col + 1], a1);
+      a = fmaf(f, red_acc[ww][g][col], a);
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const size_t slot_idx = ((size_t)seq * Hq + h0 + g) * max_splits + split;
-    *reinterpret_cast<uint32_t*>(part_o + slot_idx * D + col) = T::pack(a0 * inv, a1 * inv);
+    part_o[slot_idx * D + col] = a * inv;
     if (col == 0) {
       part_m[slot_idx] = M;
       part_l[slot_idx] = l;
@@ -290,7 +289,7 @@ constexpr int kMergeFast = 16;  // splits the merge reads in one go
 template <class T, int D>
 __global__ __launch_bounds__(64) void fa_decode_merge(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
-    const uint16_t* __restrict__ part_o, const int32_t* __restrict__ seq_lens, int Hq,
+    const float* __restrict__ part_o, const int32_t* __restrict__ seq_lens, int Hq,
     int split_tokens, int max_splits, uint16_t* __restrict__ O) {
   constexpr int PER = D / 64;
   const int h = blockIdx.x, seq = blockIdx.y;
@@ -300,6 +299,16 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
   const size_t base = ((size_t)seq * Hq + h) * max_splits;
 
   uint16_t* orow = O + ((size_t)seq * Hq + h) * D + lane * PER;
+  // This lane's PER fp32 columns of one split's o.
+  auto load_o = [&](const float* row, float (&x)[PER]) {
+    if constexpr (PER == 2) {
+      const f32x2 pr = *reinterpret_cast<const f32x2*>(row + lane * PER);
+      x[0] = pr[0];
+      x[1] = pr[1];
+    } else {
+      x[0] = row[lane];
+    }
+  };
   auto store = [&](const float (&a)[PER], float inv) {
     if constexpr (PER == 2) {
       *reinterpret_cast<uint32_t*>(orow) = T::pack(a[0] * inv, a[1] * inv);
@@ -326,16 +335,7 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
     const float lsv = mine ? part_l[base + lane] : 0.f;
     float x[kMergeFast][PER];
 #pragma unroll
-    for (int u = 0; u < kMergeFast; ++u) {
-      const uint16_t* src = part_o + (base + min(u, ns - 1)) * D + lane * PER;
-      if constexpr (PER == 2) {
-        const uint32_t pr = *reinterpret_cast<const uint32_t*>(src);
-        x[u][0] = T::lo(pr);
-        x[u][1] = T::hi(pr);
-      } else {
-        x[u][0] = T::lo((uint32_t)src[0]);
-      }
-    }
+    for (int u = 0; u < kMergeFast; ++u) load_o(part_o + (base + min(u, ns - 1)) * D, x[u]);
     float M = ms;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
@@ -376,14 +376,7 @@ __global__ __launch_bounds__(64) void fa_decode_merge(
         // and give it weight 0.
         const int j = min(j0 + u, cnt - 1);
         wj[u] = j0 + u < cnt ? __shfl(wgt, j0 + u) : 0.f;
-        const uint16_t* src = part_o + (base + s0 + j) * D + lane * PER;
-        if constexpr (PER == 2) {
-          const uint32_t pr = *reinterpret_cast<const uint32_t*>(src);
-          x[u][0] = T::lo(pr);
-          x[u][1] = T::hi(pr);
-        } else {
-          x[u][0] = T::lo((uint32_t)src[0]);
-        }
+        load_o(part_o + (base + s0 + j) * D, x[u]);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
@@ -417,8 +410,8 @@ DecodePlan decode_plan(int num_seqs, int heads_q, int heads_kv, int max_blocks_p
 }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int num_seqs, int heads_q, int dv) {
-  // part_m and part_l (fp32), then part_o (16-bit)
-  return (size_t)num_seqs * heads_q * p.max_splits * (2 * sizeof(float) + (size_t)dv * 2);
+  // part_m, part_l and part_o, all fp32
+  return (size_t)num_seqs * heads_q * p.max_splits * (2 + (size_t)dv) * sizeof(float);
 }
 
 template <class T, int D, int GW>
@@ -428,7 +421,7 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   const int shift = pow2 ? __builtin_ctz((unsigned)bs) : -1;
   float* part_m = (float*)a.workspace;
   float* part_l = part_m + (size_t)a.num_seqs * a.heads_q * p.max_splits;
-  uint16_t* part_o = (uint16_t*)(part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits);
+  float* part_o = part_l + (size_t)a.num_seqs * a.heads_q * p.max_splits;
   const float c = a.scale * kLog2e;
   dim3 grid1(a.heads_kv * p.subgroups, p.max_splits, a.num_seqs);
   auto kernel = pow2 ? &fa_decode_split<T, D, GW, true> : &fa_decode_split<T, D, GW, false>;

@@ -292,6 +292,11 @@ def paged_prefill(q, k_cache, v_cache, block_table, seq_lens, block_size: int | 
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((S, Hq, n, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", 4, dev)
+        if out.dtype != q.dtype or tuple(out.shape) != (S, Hq, n, dv):
+            raise ValueError(f"out must be {q.dtype} {(S, Hq, n, dv)}, got {out.dtype} "
+                             f"{tuple(out.shape)}")
     check(lib.fa_paged_prefill(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv, n, d,
                                dv, NB, block_table.shape[1], float(scale), 1 if causal else 0,
@@ -337,8 +342,18 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | N
     need = paged_decode_workspace_size(S, Hq, Hkv, dv, maxb, block_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        if not workspace.is_cuda or workspace.device != dev:
+            raise ValueError(f"workspace must be a device tensor on {dev}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     if out is None:
         out = torch.empty((S, Hq, dv), dtype=q.dtype, device=dev)
+    else:
+        _require(out, "out", 3, dev)
+        if out.dtype != q.dtype or tuple(out.shape) != (S, Hq, dv):
+            raise ValueError(f"out must be {q.dtype} {(S, Hq, dv)}, got {out.dtype} "
+                             f"{tuple(out.shape)}")
     check(lib.fa_paged_decode(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv, d, dv,
                               NB, maxb, float(scale), _ptr(out), _ptr(workspace),
