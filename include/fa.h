@@ -239,6 +239,31 @@ fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const
                           int num_blocks, int max_blocks_per_seq, float scale, void* o,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_paged_decode_noalloc -- fa_paged_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation, arguments and checks, with
+ * no workspace argument.  The split states live in a static device array of
+ * FA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from the
+ * moment the library's code is loaded on that GPU until the process ends; the
+ * call allocates and frees nothing.
+ *
+ * Sizes whose split states exceed FA_NOALLOC_SCRATCH_BYTES (see
+ * fa_paged_decode_workspace_size) return FA_ERR_WORKSPACE without launching.
+ * The 64-sequence, 32-head, 512-block-of-16 decode needs 17 MB of it.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one
+ * GPU (other streams, other host threads) race and give undefined results;
+ * calls ordered on one stream are safe.  The scratch of the calling thread's
+ * current device is used, so `stream` must belong to that device.
+ * FA_ERR_HIP also if the scratch address cannot be looked up.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_paged_decode_noalloc(fa_dtype dt, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int block_size, int num_seqs,
+                                  int heads_q, int heads_kv, int d, int dv, int num_blocks,
+                                  int max_blocks_per_seq, float scale, void* o, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(fa_status s);
 

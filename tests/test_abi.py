@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_fwd_partial", "fa_last_error",
                                     "fa_merge",
-                                    "fa_paged_decode", "fa_paged_decode_workspace_size",
+                                    "fa_paged_decode", "fa_paged_decode_noalloc",
+                                    "fa_paged_decode_workspace_size",
                                     "fa_paged_prefill", "fa_status_string"]
 
 
@@ -171,6 +172,40 @@ def dec(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, 
 def test_decode_rejects_before_launch(lib, kw, code):
     assert dec(lib, **kw) == code
     assert lib.fa_last_error().decode() != ""
+
+
+def dec_noalloc(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, dv=128,
+                NB=64, maxb=16, scale=0.088, o=P):
+    return lib.fa_paged_decode_noalloc(dt, q, kc, vc, bt, sl, bs, S, Hq, Hkv, d, dv, NB, maxb,
+                                       scale, o, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=9), fa.FA_ERR_INVALID),
+    (dict(bs=0), fa.FA_ERR_INVALID),
+    (dict(NB=0), fa.FA_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID),
+    (dict(d=80, dv=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=None), fa.FA_ERR_INVALID),
+    (dict(vc=MISALIGNED), fa.FA_ERR_INVALID),
+    # split states beyond the static scratch (545 MB for these sizes)
+    (dict(S=256, Hq=64, Hkv=8, maxb=2048), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects_before_launch(lib, kw, code):
+    assert dec_noalloc(lib, **kw) == code
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_decode_noalloc_empty_work_is_ok(lib):
+    assert dec_noalloc(lib, q=None, kc=None, vc=None, bt=None, sl=None, o=None, S=0) == fa.FA_OK
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
 
 
 def test_decode_workspace_size(lib):

@@ -240,12 +240,17 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int heads_q, int heads_kv, i
   return fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
 }
 
-fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
-                          int num_seqs, int heads_q, int heads_kv, int d, int dv, int num_blocks,
-                          int max_blocks_per_seq, float scale, void* o, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  g_last_error[0] = '\0';
+// Checks shared by fa_paged_decode and fa_paged_decode_noalloc.  Returns FA_OK
+// with *empty set when there is nothing to compute, else FA_OK with the plan's
+// workspace size in *need.
+static fa_status check_decode(fa_dtype dt, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int block_size, int num_seqs, int heads_q,
+                              int heads_kv, int d, int dv, int num_blocks,
+                              int max_blocks_per_seq, float scale, const void* o, bool* empty,
+                              size_t* need) {
+  *empty = false;
+  *need = 0;
   if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
   fa_status s = check_decode_sizes(num_seqs, heads_q, heads_kv, d, dv, max_blocks_per_seq,
@@ -259,14 +264,32 @@ fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const
   if ((long long)num_blocks * block_size >= (1LL << 32))
     return fail(FA_ERR_INVALID, "cache holds 2^32 or more token rows");
   if (dt == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "paged decode supports f16 and bf16");
-  if (num_seqs == 0 || heads_q == 0) return FA_OK;
+  if (num_seqs == 0 || heads_q == 0) {
+    *empty = true;
+    return FA_OK;
+  }
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
     return fail(FA_ERR_INVALID, "null pointer argument");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
   const fa::DecodePlan p =
       fa::decode_plan(num_seqs, heads_q, heads_kv, max_blocks_per_seq, block_size);
-  const size_t need = fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
+  *need = fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
+  return FA_OK;
+}
+
+fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, int block_size,
+                          int num_seqs, int heads_q, int heads_kv, int d, int dv, int num_blocks,
+                          int max_blocks_per_seq, float scale, void* o, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  bool empty;
+  size_t need;
+  const fa_status s = check_decode(dt, q, k_cache, v_cache, block_table, seq_lens, block_size,
+                                   num_seqs, heads_q, heads_kv, d, dv, num_blocks,
+                                   max_blocks_per_seq, scale, o, &empty, &need);
+  if (s != FA_OK || empty) return s;
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                 need);
@@ -277,6 +300,34 @@ fa_status fa_paged_decode(fa_dtype dt, const void* q, const void* k_cache, const
                    scale, o, workspace, stream};
   const hipError_t e = fa::launch_decode(a);
   if (e != hipSuccess) return hip_fail(e, "fa_paged_decode launch");
+  return FA_OK;
+}
+
+fa_status fa_paged_decode_noalloc(fa_dtype dt, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int block_size, int num_seqs,
+                                  int heads_q, int heads_kv, int d, int dv, int num_blocks,
+                                  int max_blocks_per_seq, float scale, void* o, void* stream) {
+  g_last_error[0] = '\0';
+  bool empty;
+  size_t need;
+  const fa_status s = check_decode(dt, q, k_cache, v_cache, block_table, seq_lens, block_size,
+                                   num_seqs, heads_q, heads_kv, d, dv, num_blocks,
+                                   max_blocks_per_seq, scale, o, &empty, &need);
+  if (s != FA_OK || empty) return s;
+  if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES)
+    return fail(FA_ERR_WORKSPACE,
+                "these sizes need %zu bytes of split states, above the %zu-byte static scratch "
+                "of fa_paged_decode_noalloc (use fa_paged_decode with a workspace)",
+                need, (size_t)FA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  hipError_t e = fa::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "fa_paged_decode_noalloc scratch lookup");
+  fa::DecodeArgs a{(int)dt, q,        k_cache,  v_cache,    block_table,        seq_lens,
+                   block_size, num_seqs, heads_q, heads_kv, d, num_blocks, max_blocks_per_seq,
+                   scale, o, scratch, stream};
+  e = fa::launch_decode(a);
+  if (e != hipSuccess) return hip_fail(e, "fa_paged_decode_noalloc launch");
   return FA_OK;
 }
 

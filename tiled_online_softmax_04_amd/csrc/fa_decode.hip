@@ -41,10 +41,43 @@
 //    final one: for outputs in [2, 4) in bf16 the two together can exceed
 //    1e-2.)
 
+#include <mutex>
+
+#include "../../include/fa.h"
 #include "fa_common.h"
 #include "fa_launch.h"
 
+// The workspace of fa_paged_decode_noalloc: the split states in a static
+// device array.  Every GPU the library runs on holds its own copy from the
+// moment the code object is loaded there until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it only stands in
+// for the symbol); it passes the device address decode_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
 namespace fa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};  // per device; null until looked up
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 constexpr int kDecWaves = 8;  // per split: 8 chunks of 16 tokens each in flight
 constexpr int kDecThreads = 64 * kDecWaves;

@@ -98,5 +98,9 @@ DecodePlan decode_plan(int num_seqs, int heads_q, int heads_kv, int max_blocks_p
                        int block_size);
 size_t decode_workspace_bytes(const DecodePlan& p, int num_seqs, int heads_q, int dv);
 hipError_t launch_decode(const DecodeArgs& a);
+// Device address of the calling thread's current device's copy of the static
+// scratch array that fa_paged_decode_noalloc uses as its workspace (looked up
+// once per device).
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace fa

@@ -63,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                     _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     ctypes.c_float, _c_void_p, _c_void_p, ctypes.c_size_t,
                                     _c_void_p]
+    lib.fa_paged_decode_noalloc.restype = _c_int
+    lib.fa_paged_decode_noalloc.argtypes = [_c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_int, _c_int, ctypes.c_float, _c_void_p,
+                                            _c_void_p]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [_c_int]
     lib.fa_last_error.restype = ctypes.c_char_p
@@ -310,13 +315,10 @@ def paged_decode_workspace_size(num_seqs, heads_q, heads_kv, dv, max_blocks_per_
                                                             max_blocks_per_seq, block_size))
 
 
-def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | None = None,
-                 scale: float | None = None, out=None, workspace=None, stream=None):
-    """One query token per sequence over a paged cache.  q [S, Hq, d];
-    k_cache [NB, bs, Hkv, d]; v_cache [NB, bs, Hkv, dv]; block_table int32
-    [S, max_blocks]; seq_lens int32 [S].  scale defaults to 1/sqrt(d)."""
+def _decode_shapes(q, k_cache, v_cache, block_table, seq_lens, block_size, out):
+    """Checks shared by the two decode entry points; returns the sizes and the
+    output tensor (allocated when `out` is None)."""
     import torch
-    lib = load_library()
     dev = q.device
     _require(q, "q", 3, dev)
     _require(k_cache, "k_cache", 4, dev)
@@ -336,17 +338,6 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | N
         raise ValueError("cache shapes do not match q / block_size")
     if block_table.shape[0] != S or seq_lens.shape[0] != S:
         raise ValueError("block_table / seq_lens batch mismatch")
-    maxb = block_table.shape[1]
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    need = paged_decode_workspace_size(S, Hq, Hkv, dv, maxb, block_size)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-    else:
-        if not workspace.is_cuda or workspace.device != dev:
-            raise ValueError(f"workspace must be a device tensor on {dev}")
-        if not workspace.is_contiguous():
-            raise ValueError("workspace must be contiguous")
     if out is None:
         out = torch.empty((S, Hq, dv), dtype=q.dtype, device=dev)
     else:
@@ -354,8 +345,50 @@ def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | N
         if out.dtype != q.dtype or tuple(out.shape) != (S, Hq, dv):
             raise ValueError(f"out must be {q.dtype} {(S, Hq, dv)}, got {out.dtype} "
                              f"{tuple(out.shape)}")
+    return S, Hq, Hkv, d, dv, NB, block_size, block_table.shape[1], out
+
+
+def paged_decode(q, k_cache, v_cache, block_table, seq_lens, block_size: int | None = None,
+                 scale: float | None = None, out=None, workspace=None, stream=None):
+    """One query token per sequence over a paged cache.  q [S, Hq, d];
+    k_cache [NB, bs, Hkv, d]; v_cache [NB, bs, Hkv, dv]; block_table int32
+    [S, max_blocks]; seq_lens int32 [S].  scale defaults to 1/sqrt(d)."""
+    import torch
+    lib = load_library()
+    S, Hq, Hkv, d, dv, NB, block_size, maxb, out = _decode_shapes(
+        q, k_cache, v_cache, block_table, seq_lens, block_size, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = paged_decode_workspace_size(S, Hq, Hkv, dv, maxb, block_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        if not workspace.is_cuda or workspace.device != q.device:
+            raise ValueError(f"workspace must be a device tensor on {q.device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     check(lib.fa_paged_decode(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                               _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv, d, dv,
                               NB, maxb, float(scale), _ptr(out), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+# Bytes of the static scratch behind paged_decode_noalloc (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, block_size: int | None = None,
+                         scale: float | None = None, out=None, stream=None):
+    """paged_decode through fa_paged_decode_noalloc: the split states live in
+    the library's static per-GPU scratch, so the call allocates nothing when
+    `out` is given.  Calls that overlap on one GPU race (one scratch per GPU)."""
+    lib = load_library()
+    S, Hq, Hkv, d, dv, NB, block_size, maxb, out = _decode_shapes(
+        q, k_cache, v_cache, block_table, seq_lens, block_size, out)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    check(lib.fa_paged_decode_noalloc(_dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(block_table), _ptr(seq_lens), block_size, S, Hq, Hkv,
+                                      d, dv, NB, maxb, float(scale), _ptr(out), _stream(stream)))
     return out
