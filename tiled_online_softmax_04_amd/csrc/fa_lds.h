@@ -13,7 +13,8 @@ namespace fa {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Row placement of the K tile inside each 32-row block.  The accumulator of a
 // 32x32 MFMA (any input type) gives lane l, element i the row
@@ -26,23 +27,72 @@ __device__ __forceinline__ int kappa(int r) {
   return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 0xC);
 }
 
-// Raw buffer descriptor over [base, base + bytes).  Loads at offsets outside
-// the range (including "negative" offsets, which wrap past 2^31) return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+// Raw buffer descriptor over [base, base + bytes) as four words, for
+// dma16_untracked: base address, no stride, `bytes` of range.  Loads at
+// offsets outside the range (including "negative" offsets, which wrap past
+// 2^31) return zeros.  Wave-uniform.
+__device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
 }
 
 // 16 bytes per lane straight from a buffer into LDS: the wave's 64 lanes fill
-// 1 KB at `lds_base` in lane order (lane l at lds_base + 16*l).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_char* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+// 1 KB at `lds_addr` in lane order (lane l at lds_addr + 16 l).  Written out
+// as instructions, so that the compiler does not count it among its own
+// memory operations.  The compiler treats a transposing LDS read
+// as possibly overlapping any LDS write in flight from a buffer load and would
+// otherwise wait for every tile load before each such read; here the caller's
+// explicit vmcnt waits (before every barrier) are what order the tile loads
+// against the reads.  The instruction writes no register (its destination is
+// LDS), m0 is restored before the block ends, and the one wait state between
+// the m0 write and its use is included.
+__device__ __forceinline__ void dma16_untracked(u32x4 rsrc, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rsrc), "s"(lds_addr)
+      : "memory");
 }
 
 // The same from a 64-bit global address per lane (used where the rows of a
-// tile come from scattered cache blocks).
-__device__ __forceinline__ void gdma16(const void* src, lds_char* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+// tile come from scattered cache blocks), written out for the same reason as
+// dma16_untracked: no register written, m0 restored, the wait state included.
+__device__ __forceinline__ void gdma16_untracked(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+// Transposing LDS reads through the compiler's builtins (the compiler waits
+// for them before their results are used).
+//  16-bit: within each 16 lanes, lane 4r+t names row r, columns 4t..4t+3;
+//          lane c receives column c of the 4 rows.
+//  8-bit:  within each 16 lanes, lane 2r+t names row r, bytes 8t..8t+7 of a
+//          16-byte chunk; lane c receives byte c of that chunk from each of
+//          the 8 rows (row r in byte r).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t lds_addr) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (lds_i16x4*)(uintptr_t)lds_addr));
+}
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t lds_addr) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                       (lds_i32x2*)(uintptr_t)lds_addr));
 }
 
 // s_waitcnt lgkmcnt(0) (vmcnt, expcnt untouched).

@@ -5,15 +5,17 @@
 // keeps them resident in VGPRs as MFMA operands ("Q 常驻片上寄存器", 10100.com
 // section 7).  64-key K/V tiles stream through a ring of LDS stages: each
 // wave moves its share of a tile with buffer loads that write LDS directly (no
-// VGPR round trip).  Two tiles are computed between barriers from one half of
-// a four-stage ring while the next two land in the other half (the paged form:
-// one tile per barrier, three stages, two tiles ahead).
-// Per tile the wave forms S^T = K Q^T with v_mfma_f32_32x32x16, applies the
-// online-softmax update of the same section (running max, rescale of the
-// history by exp(m_old - m_new), running sum) and accumulates O^T += V^T P^T
-// with a second MFMA whose V^T operands come from transposing LDS reads.  Tiles
-// wholly above the causal diagonal or wholly inside a left pad are never
-// visited (10100.com section 6).
+// VGPR round trip).  Per tile the wave forms S^T = K Q^T with
+// v_mfma_f32_32x32x16, applies the online-softmax update of the same section
+// (running max, rescale of the history by exp(m_old - m_new), running sum) and
+// accumulates O^T += V^T P^T with a second MFMA whose V^T operands come from
+// transposing LDS reads.  Contiguous K/V run as a software pipeline over the
+// tiles (one barrier per tile, four stages): tile t+1's scores are formed
+// beside tile t's exponentials, and tile t's P.V beside tile t+1's row max.
+// The paged form keeps one tile per barrier, three stages, two tiles ahead,
+// with the softmax between the two products.  Tiles wholly above the causal
+// diagonal or wholly inside a left pad are never visited (10100.com
+// section 6).
 //
 // Why S^T rather than S: in the 32x32 MFMA accumulator each lane holds one
 // column and 16 rows.  With keys as rows and queries as columns every lane
@@ -53,17 +55,9 @@ constexpr int kThreads = 64 * kWaves;
 // LDS ring of K/V tiles: tile t is computed while tiles t+1 .. t+kStages-1 land.
 constexpr int kStages = FA_PREFILL_STAGES;
 static_assert(kStages == 2 || kStages == 3, "ring depth");
-// Tiles computed between two barriers.  With more than one, the ring holds
-// 2 * kGroup stages: one half is computed while the next group lands in the
-// other half.  The paged form keeps one tile per barrier (its block table
-// shares LDS with the ring).
-#ifndef FA_PREFILL_GROUP
-#define FA_PREFILL_GROUP 2
-#endif
-constexpr int kGroup = FA_PREFILL_GROUP;
-constexpr int ring_stages(bool paged) {
-  return (!paged && kGroup > 1) ? 2 * kGroup : kStages;
-}
+// LDS stages of the K/V ring: three for the paged form (one tile per barrier,
+// two tiles ahead), four for the contiguous form's pipeline.
+constexpr int ring_stages(bool paged) { return paged ? kStages : 4; }
 
 template <int D>
 struct Geo {
@@ -94,18 +88,6 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// Transposing LDS read: within each 16 lanes, lane 4r+t names row r, columns
-// 4t..4t+3; lane c receives column c of the 4 rows.  Issued from inline asm so
-// that the byte offset OFF lands in the instruction's offset field; the result
-// is valid only after wait_lgkm0() followed by reg_barrier() on it.
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_read_tr16_at(uint32_t lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF)
-               : "memory");
-  return r;
-}
-
 // PARTIAL: attend only to keys in [key_begin, key_end) and write the result
 // normalised over that range as float32 (Of) together with the natural-log
 // softmax denominator of the range (Lse), instead of the final O.
@@ -123,7 +105,6 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     int m, int key_begin, int key_end, int q_tiles, int total, float c,
     const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks) {
   using G = Geo<D>;
-  constexpr int kGrp = PAGED ? 1 : kGroup;
   constexpr int kRing = ring_stages(PAGED);
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -185,8 +166,6 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   // back as zeros, so no tile ever needs clamping and padding contents never
   // reach the arithmetic.
   const uint32_t kv_bytes = (uint32_t)max(key_hi - key_lo, 0) * (uint32_t)(D * 2);
-  const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(Kh + (size_t)key_lo * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(Vh + (size_t)key_lo * D, kv_bytes);
 
   // DMA of a tile into a ring stage.  Lane l of a wave DMA fills LDS row
   // p = first + l / kChunks, physical chunk l % kChunks, and fetches the key
@@ -206,7 +185,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     dma_key[i] = klocal;
     dma_col[i] = chunk * 8;
   }
-  const __amdgpu_buffer_rsrc_t rsrc_dma = dma_v ? rsrc_v : rsrc_k;
+  const u32x4 rsrc_dma_words =
+      make_rsrc_words(dma_v ? Vh + (size_t)key_lo * D : Kh + (size_t)key_lo * D, kv_bytes);
   lds_char* const lds = (lds_char*)smem;
   const int dma_lds0 = (dma_v ? G::kTileElems : 0) * 2 +
                        (w * G::kDmaPerWave - (dma_v ? G::kDmaPerTile : 0)) *
@@ -233,19 +213,26 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
         tok = tok < kv_end ? tok : kv_end - 1;
         const int blk = bs_shift >= 0 ? tok >> bs_shift : tok / bs;
         const size_t row = (size_t)bt_s[blk] * (size_t)bs + (size_t)(tok - blk * bs);
-        gdma16(cache_dma + (row * Hkv + hkv) * D + dma_col[i], dst + i * G::kRowsPerDma * D * 2);
+        gdma16_untracked(cache_dma + (row * Hkv + hkv) * D + dma_col[i],
+                         (uint32_t)__builtin_amdgcn_readfirstlane(
+                             (uint32_t)(uintptr_t)(dst + i * G::kRowsPerDma * D * 2)));
       }
     } else {
       const uint32_t tile_off = (uint32_t)((t * kBc - key_lo) * D * 2);
+      const uint32_t lds0 =
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
 #pragma unroll
       for (int i = 0; i < G::kDmaPerWave; ++i)
-        dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D * 2);
+        dma16_untracked(rsrc_dma_words, tile_off + dma_off[i],
+                        lds0 + (uint32_t)(i * G::kRowsPerDma * D * 2));
     }
   };
 
+  if constexpr (PAGED) {
 #pragma unroll
-  for (int i = 0; i < (kGrp > 1 ? kGrp : kStages - 1); ++i)
-    if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+    for (int i = 0; i < kStages - 1; ++i)
+      if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+  }
 
   // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive d.
   u32x4 qT[kNT][G::kQSteps];
@@ -281,173 +268,160 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       v_off[t2] = (uint32_t)(key * D + (((4 * t2 + chunk) ^ v_swz<D>(key)) * 8) + (i & 1) * 4) * 2u;
   }
 
-  wait_vm_lgkm0<0>();
-  bare_barrier();
+  if constexpr (PAGED) {
+    wait_vm_lgkm0<0>();
+    bare_barrier();
 
-  // One tile from ring stage st: scores, online softmax, P.V.
-  auto tile = [&](int t, int st) __attribute__((always_inline)) {
-    const int j0 = t * kBc;
-    // Whole wave above the causal diagonal, or wholly padding: nothing to add.
-    const bool wave_idle = (CAUSAL && j0 > wq0 + qoff + kQPerWave - 1) ||
-                           (RAGGED && wq0 + kQPerWave - 1 < pad) ||
-                           (PAGED && wq0 + qoff + kQPerWave - 1 < 0);
-    if (!wave_idle) {
-      const lds_char* Ks = lds + st * G::kStageElems * 2;
-      const lds_char* Vs = Ks + G::kTileElems * 2;
+    // One tile from ring stage st: scores, online softmax, P.V.
+    auto tile = [&](int t, int st) __attribute__((always_inline)) {
+      const int j0 = t * kBc;
+      // Whole wave above the causal diagonal, or wholly padding: nothing to add.
+      const bool wave_idle = (CAUSAL && j0 > wq0 + qoff + kQPerWave - 1) ||
+                             (RAGGED && wq0 + kQPerWave - 1 < pad) ||
+                             (PAGED && wq0 + qoff + kQPerWave - 1 < 0);
+      if (!wave_idle) {
+        const lds_char* Ks = lds + st * G::kStageElems * 2;
+        const lds_char* Vs = Ks + G::kTileElems * 2;
 
-      // S^T[key][query]: 64 keys (two 32-row tiles) x kQPerWave queries.
-      f32x16 sacc[2][kNT];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) sacc[0][nt] = sacc[1][nt] = f32x16{};
-      // K operands in batches of four k-steps: a batch's LDS reads are all
-      // issued before its MFMAs, so the MFMAs do not wait out one read's
-      // latency each (left to itself the compiler pairs every read with the
-      // MFMA that uses it).
-      constexpr int KB = G::kQSteps < 4 ? G::kQSteps : 4;
-      static_assert(G::kQSteps % KB == 0, "batch");
-#pragma unroll
-      for (int kb = 0; kb < G::kQSteps; kb += KB) {
-        u32x4 ka[KB][2];
-#pragma unroll
-        for (int u = 0; u < KB; ++u) {
-          ka[u][0] = *(const lds_u32x4*)(Ks + k_off[kb + u]);
-          ka[u][1] = *(const lds_u32x4*)(Ks + k_off[kb + u] + 32 * D * 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < KB; ++u)
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            sacc[0][nt] = T::mfma32x32x16(ka[u][0], qT[nt][kb + u], sacc[0][nt]);
-            sacc[1][nt] = T::mfma32x32x16(ka[u][1], qT[nt][kb + u], sacc[1][nt]);
+        // S^T[key][query]: 64 keys (two 32-row tiles) x kQPerWave queries.
+        f32x16 sacc[2][kNT];
+  #pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) sacc[0][nt] = sacc[1][nt] = f32x16{};
+        // K operands in batches of four k-steps: a batch's LDS reads are all
+        // issued before its MFMAs, so the MFMAs do not wait out one read's
+        // latency each (left to itself the compiler pairs every read with the
+        // MFMA that uses it).
+        constexpr int KB = G::kQSteps < 4 ? G::kQSteps : 4;
+        static_assert(G::kQSteps % KB == 0, "batch");
+  #pragma unroll
+        for (int kb = 0; kb < G::kQSteps; kb += KB) {
+          u32x4 ka[KB][2];
+  #pragma unroll
+          for (int u = 0; u < KB; ++u) {
+            ka[u][0] = *(const lds_u32x4*)(Ks + k_off[kb + u]);
+            ka[u][1] = *(const lds_u32x4*)(Ks + k_off[kb + u] + 32 * D * 2);
           }
-      }
-
-      // V^T operands through transposing reads: 2 reads per (k-step j, dv tile).
-      const uint32_t vs_addr = (uint32_t)(uintptr_t)Vs;
-      uint32_t va[G::kOTiles];
-#pragma unroll
-      for (int t2 = 0; t2 < G::kOTiles; ++t2) va[t2] = vs_addr + v_off[t2];
-      u32x2 vr[4][G::kOTiles][2];
-      auto issue_v = [&](auto J) {
-        constexpr int j = decltype(J)::value;
-#pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-          vr[j][t2][0] = ds_read_tr16_at<(16 * j) * D * 2>(va[t2]);
-          vr[j][t2][1] = ds_read_tr16_at<(16 * j + 4) * D * 2>(va[t2]);
-        }
-      };
-      auto mma_v = [&](auto J, const u32x4 (&pbr)[kNT][4]) {
-        constexpr int j = decltype(J)::value;
-#pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-          reg_barrier(vr[j][t2][0]);
-          reg_barrier(vr[j][t2][1]);
-          const u32x4 a = {vr[j][t2][0][0], vr[j][t2][0][1], vr[j][t2][1][0], vr[j][t2][1][1]};
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) acc[t2][nt] = T::mfma32x32x16(a, pbr[nt][j], acc[t2][nt]);
-        }
-      };
-      static_for<0, 2>([&](auto J) { issue_v(J); });
-
-      // Mask only tiles that straddle the diagonal, the pad or the end of K
-      // (a real branch: most tiles need no mask at all).
-      const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0 + qoff) || (j0 + kBc > key_hi) ||
-                             (j0 < key_lo);
-      if (__builtin_expect(need_mask, 0)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = 16 * (i >> 3) + 8 * hf + (i & 7);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const int key = j0 + 32 * mt + kk;
-            const bool kbad = key >= key_hi || key < key_lo;
-#pragma unroll
+          __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+          for (int u = 0; u < KB; ++u)
+  #pragma unroll
             for (int nt = 0; nt < kNT; ++nt) {
-              const bool bad = kbad || (CAUSAL && key > qrow[nt] + qoff);
-              sacc[mt][nt][i] = bad ? -__builtin_inff() : sacc[mt][nt][i];
+              sacc[0][nt] = T::mfma32x32x16(ka[u][0], qT[nt][kb + u], sacc[0][nt]);
+              sacc[1][nt] = T::mfma32x32x16(ka[u][1], qT[nt][kb + u], sacc[1][nt]);
+            }
+        }
+
+        // V^T operands through transposing reads: 2 reads per (k-step j, dv tile).
+        const uint32_t vs_addr = (uint32_t)(uintptr_t)Vs;
+        uint32_t va[G::kOTiles];
+  #pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) va[t2] = vs_addr + v_off[t2];
+        u32x2 vr[4][G::kOTiles][2];
+        auto issue_v = [&](auto J) {
+          constexpr int j = decltype(J)::value;
+  #pragma unroll
+          for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+            vr[j][t2][0] = lds_read_tr16(va[t2] + (16 * j) * D * 2);
+            vr[j][t2][1] = lds_read_tr16(va[t2] + (16 * j + 4) * D * 2);
+          }
+        };
+        auto mma_v = [&](auto J, const u32x4 (&pbr)[kNT][4]) {
+          constexpr int j = decltype(J)::value;
+  #pragma unroll
+          for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+            const u32x4 a = {vr[j][t2][0][0], vr[j][t2][0][1], vr[j][t2][1][0], vr[j][t2][1][1]};
+  #pragma unroll
+            for (int nt = 0; nt < kNT; ++nt) acc[t2][nt] = T::mfma32x32x16(a, pbr[nt][j], acc[t2][nt]);
+          }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 2>([&](auto J) { issue_v(J); });
+        __builtin_amdgcn_sched_barrier(0);  // the V^T reads go out here
+
+        // Mask only tiles that straddle the diagonal, the pad or the end of K
+        // (a real branch: most tiles need no mask at all).
+        const bool need_mask = (CAUSAL && j0 + kBc - 1 > wq0 + qoff) || (j0 + kBc > key_hi) ||
+                               (j0 < key_lo);
+        if (__builtin_expect(need_mask, 0)) {
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 16 * (i >> 3) + 8 * hf + (i & 7);
+  #pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+              const int key = j0 + 32 * mt + kk;
+              const bool kbad = key >= key_hi || key < key_lo;
+  #pragma unroll
+              for (int nt = 0; nt < kNT; ++nt) {
+                const bool bad = kbad || (CAUSAL && key > qrow[nt] + qoff);
+                sacc[mt][nt][i] = bad ? -__builtin_inff() : sacc[mt][nt][i];
+              }
             }
           }
         }
-      }
 
-      // Online softmax: tile row max (lane-local + the partner lane 32 away).
-      float mx[kNT];
-      bool raise = false;
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        float a = fmaxf(sacc[0][nt][0], sacc[0][nt][1]);
-#pragma unroll
-        for (int i = 2; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[0][nt][i], sacc[0][nt][i + 1]));
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[1][nt][i], sacc[1][nt][i + 1]));
-        mx[nt] = max_xor32(a) * c;
-        raise = raise || mx[nt] > m_run[nt] + kSlack;
-      }
-      // Raise the running max only when the tile beats it by more than kSlack
-      // (wave-uniform branch).  Weights are then at most 2^kSlack, and acc and
-      // l always share the same m, so O = acc / l is unchanged.
-      if (__builtin_expect(__any(raise), 0)) {
-        // A real branch: without the barrier the compiler executes the
-        // rescale on every tile with alpha = 1.
-        asm volatile("" ::: "memory");
-#pragma unroll
+        // Online softmax: tile row max (lane-local + the partner lane 32 away).
+        float mx[kNT];
+        bool raise = false;
+  #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-          const float m_new = fmaxf(m_run[nt], mx[nt]);
-          const float alpha = fast_exp2(m_run[nt] - m_new);
-          l_run[nt] *= alpha;
-#pragma unroll
-          for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] *= alpha;
-          m_run[nt] = m_new;
+          float a = fmaxf(sacc[0][nt][0], sacc[0][nt][1]);
+  #pragma unroll
+          for (int i = 2; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[0][nt][i], sacc[0][nt][i + 1]));
+  #pragma unroll
+          for (int i = 0; i < 16; i += 2) a = fmaxf(a, fmaxf(sacc[1][nt][i], sacc[1][nt][i + 1]));
+          mx[nt] = max_xor32(a) * c;
+          raise = raise || mx[nt] > m_run[nt] + kSlack;
         }
-      }
-
-      // p = exp2(S*c - m) as the B operand of O^T += V^T P^T.  The running
-      // sum adds the same rounded weights the MFMA uses (two per v_dot2).
-      u32x4 pb[kNT][4];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * (j & 1) + 2 * e;
-            const float p0 = fast_exp2(fmaf(sacc[j >> 1][nt][i], c, -m_run[nt]));
-            const float p1 = fast_exp2(fmaf(sacc[j >> 1][nt][i + 1], c, -m_run[nt]));
-            pb[nt][j][e] = T::pack(p0, p1);
-            if (e & 1) ps1 = T::add_pair(pb[nt][j][e], ps1);
-            else ps0 = T::add_pair(pb[nt][j][e], ps0);  // two chains for latency
+        // Raise the running max only when the tile beats it by more than kSlack
+        // (wave-uniform branch).  Weights are then at most 2^kSlack, and acc and
+        // l always share the same m, so O = acc / l is unchanged.
+        if (__builtin_expect(__any(raise), 0)) {
+          // A real branch: without the barrier the compiler executes the
+          // rescale on every tile with alpha = 1.
+          asm volatile("" ::: "memory");
+  #pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) {
+            const float m_new = fmaxf(m_run[nt], mx[nt]);
+            const float alpha = fast_exp2(m_run[nt] - m_new);
+            l_run[nt] *= alpha;
+  #pragma unroll
+            for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][nt] *= alpha;
+            m_run[nt] = m_new;
           }
         }
-        l_run[nt] += ps0 + ps1;
+
+        // p = exp2(S*c - m) as the B operand of O^T += V^T P^T.  The running
+        // sum adds the same rounded weights the MFMA uses (two per v_dot2).
+        u32x4 pb[kNT][4];
+  #pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          float ps0 = 0.f, ps1 = 0.f;
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 8 * (j & 1) + 2 * e;
+              const float p0 = fast_exp2(fmaf(sacc[j >> 1][nt][i], c, -m_run[nt]));
+              const float p1 = fast_exp2(fmaf(sacc[j >> 1][nt][i + 1], c, -m_run[nt]));
+              pb[nt][j][e] = T::pack(p0, p1);
+              if (e & 1) ps1 = T::add_pair(pb[nt][j][e], ps1);
+              else ps0 = T::add_pair(pb[nt][j][e], ps0);  // two chains for latency
+            }
+          }
+          l_run[nt] += ps0 + ps1;
+        }
+
+        // O^T += V^T P^T.  k-steps 0, 1 of V^T were requested before the
+        // softmax; 2, 3 go out now and land during the first half of the MFMAs.
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<2, 4>([&](auto J) { issue_v(J); });
+        __builtin_amdgcn_sched_barrier(0);  // the V^T reads go out here
+        wait_lgkm0();
+        static_for<0, 2>([&](auto J) { mma_v(J, pb); });
+        wait_lgkm0();
+        static_for<2, 4>([&](auto J) { mma_v(J, pb); });
       }
-
-      // O^T += V^T P^T.  k-steps 0, 1 of V^T were requested before the
-      // softmax; 2, 3 go out now and land during the first half of the MFMAs.
-      static_for<2, 4>([&](auto J) { issue_v(J); });
-      wait_lgkm0();
-      static_for<0, 2>([&](auto J) { mma_v(J, pb); });
-      wait_lgkm0();
-      static_for<2, 4>([&](auto J) { mma_v(J, pb); });
-    }
-  };
-
-  if constexpr (kGrp > 1) {
-    // kGrp tiles from one half of the ring while the next kGrp land in the
-    // other half; one barrier per group.
-    for (int t = t_begin; t < t_end; t += kGrp) {
-      const int it = t - t_begin;
-#pragma unroll
-      for (int g = 0; g < kGrp; ++g)
-        if (t + kGrp + g < t_end) issue_tile(t + kGrp + g, (it + kGrp + g) % kRing);
-#pragma unroll
-      for (int g = 0; g < kGrp; ++g)
-        if (t + g < t_end) tile(t + g, (it + g) % kRing);
-      wait_vm_lgkm0<0>();
-      bare_barrier();
-    }
-  } else {
+    };
     for (int t = t_begin; t < t_end; ++t) {
       const int it = t - t_begin;
       // Refill the stage read in the previous iteration with tile t+kStages-1.
@@ -462,6 +436,309 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
         wait_vm_lgkm0<0>();
       }
       bare_barrier();
+    }
+  } else {
+    // ---------------------------------------------------------------------
+    // Contiguous K/V: a software pipeline over key tiles, one barrier per
+    // tile, four LDS stages (tiles t and t+1 in use, t+2 landing, t+3 being
+    // issued).  Each step issues the S^T MFMAs of tile t+1 beside tile t's
+    // exponentials, packing and row sums, then tile t's P.V MFMAs beside
+    // tile t+1's row max, running-max update and exp2 arguments, so that a
+    // wave's vector work sits between its own MFMAs (measured on gfx950: a
+    // few ordinary VALU instructions between two MFMAs of one wave cost no
+    // MFMA time; exponentials cost about half their issue time).
+    // ---------------------------------------------------------------------
+    static_assert(kNT == 1, "the pipelined loop takes 32 queries per wave");
+    constexpr int kRingP = 4;
+    static_assert(ring_stages(false) == kRingP, "LDS ring of the pipelined loop");
+    // Tiles this wave computes: [t_begin, t_wave_end).  Later tiles lie wholly
+    // above its causal diagonal; a wave of padding rows or rows past n
+    // computes none.  It still moves its share of every tile and meets every
+    // barrier.
+    int t_wave_end = t_end;
+    if (wq0 >= n) t_wave_end = t_begin;
+    if constexpr (CAUSAL) t_wave_end = min(t_wave_end, (wq0 + qoff + kQPerWave - 1) / kBc + 1);
+    if constexpr (RAGGED)
+      if (wq0 + kQPerWave - 1 < pad) t_wave_end = t_begin;
+    t_wave_end = __builtin_amdgcn_readfirstlane(max(t_wave_end, t_begin));
+
+    // The query loads above go out before the first tiles.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+    // Loads complete in issue order: at most the DMAs of the tiles after
+    // t_begin may stay in flight.
+    {
+      const int after = min(2, t_end - t_begin - 1);
+      if (after >= 2) wait_vm_lgkm0<2 * G::kDmaPerWave>();
+      else if (after == 1) wait_vm_lgkm0<G::kDmaPerWave>();
+      else wait_vm_lgkm0<0>();
+    }
+    bare_barrier();
+
+    // LDS byte offsets of the MFMA operands from one register each.  The K
+    // chunk of lane ql at k-step ks is (2 ks + hf) XOR the row's swizzle, so
+    // its offset is k_off[0] ^ (ks << 5); the transposing V read of column
+    // tile t2 sits at v_off[0] ^ (t2 << 6).  The XORed bits lie below the row
+    // bits (rows of 128 or 256 bytes) and above the lane's own chunk bits,
+    // and stage bases are multiples of 8 KB, so base + off ^ x = (base + off) ^ x.
+    static_assert(D == 128 || D == 64, "head dims");
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+    // S^T[key][query] of tile t from its ring stage: 64 keys (two 32-row
+    // tiles) x 32 queries (the first tile, before the pipeline starts).
+    auto scores = [&](int t, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+      const uint32_t kb =
+          lds_base + ((t - t_begin) & (kRingP - 1)) * G::kStageElems * 2 + k_off[0];
+      sc[0] = sc[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < G::kQSteps; ++ks) {
+        const uint32_t ka_addr = kb ^ (uint32_t)(ks << 5);
+        const u32x4 a0 = *(const lds_u32x4*)(uintptr_t)ka_addr;
+        const u32x4 a1 = *(const lds_u32x4*)(uintptr_t)(ka_addr + 32 * D * 2);
+        sc[0] = T::mfma32x32x16(a0, qT[0][ks], sc[0]);
+        sc[1] = T::mfma32x32x16(a1, qT[0][ks], sc[1]);
+      }
+    };
+
+    // Masked scores of a tile that straddles the diagonal, the pad or the
+    // ends of the key range become -inf.
+    auto mask = [&](int t, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+      const int j0 = t * kBc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 16 * (i >> 3) + 8 * hf + (i & 7);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int key = j0 + 32 * mt + kk;
+          const bool bad = key >= key_hi || key < key_lo || (CAUSAL && key > qrow[0] + qoff);
+          sc[mt][i] = bad ? -__builtin_inff() : sc[mt][i];
+        }
+      }
+    };
+
+    // Row max of a tile's scores, the running-max update, and the exp2
+    // arguments s * c - m written over the scores.  The running max moves
+    // only when the tile beats it by more than kSlack, so weights stay below
+    // 2^kSlack; acc and l always share m, so O = acc / l does not depend on
+    // where m sits.  Returns whether some row of the wave moved its max
+    // (then acc and l must be rescaled by exp2(m_old - m_new)).
+    const float c_scale = c;
+    auto softmax_args = [&](f32x16 (&sc)[2], bool live, float& m_new)
+                            __attribute__((always_inline)) {
+      float a = fmaxf(sc[0][0], sc[0][1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) a = fmaxf(a, fmaxf(sc[0][i], sc[0][i + 1]));
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) a = fmaxf(a, fmaxf(sc[1][i], sc[1][i + 1]));
+      const float mxc = max_xor32(a) * c;
+      const bool raise = live && mxc > m_run[0] + kSlack;
+      m_new = raise ? mxc : m_run[0];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[mt][i] = fmaf(sc[mt][i], c, -m_new);
+      return raise;
+    };
+    auto rescale = [&](float m_new) __attribute__((always_inline)) {
+      const float alpha = fast_exp2(m_run[0] - m_new);  // 1 for rows that kept m
+      l_run[0] *= alpha;
+#pragma unroll
+      for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2][0] *= alpha;
+    };
+
+    // One step of the pipeline.  On entry sa holds tile t's exp2 arguments
+    // (formed in the step before, or the prologue).
+    //  block A: tile t+1's S^T MFMAs beside tile t's weights p = exp2(arg),
+    //           rounded to the input type as the B operand of the P.V MFMA,
+    //           and their row sums (l adds the same rounded weights);
+    //  block C: tile t's P.V MFMAs beside tile t+1's row max and arguments;
+    //  then the rare rescale branch.
+    // The instruction order inside each block is fixed by scheduling fences:
+    // after every MFMA comes one slice of the vector work, and the LDS
+    // operand reads run four (K) or two (V) k-steps ahead of their MFMAs, so
+    // that the two waves of a SIMD keep the matrix core fed.  The last tile
+    // of a wave still forms the scores of the stage after it (stale LDS,
+    // never used): one surplus S^T product per wave and Q tile buys a
+    // straight-line step.
+    constexpr int kSlotsA = 2 * G::kQSteps;   // MFMAs of block A (16 or 8)
+    constexpr int kSlotsC = 4 * G::kOTiles;   // MFMAs of block C (16 or 8)
+    constexpr int kKpf = G::kQSteps < 4 ? G::kQSteps : 4;  // K k-steps ahead
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](int t, f32x16 (&sa)[2], f32x16 (&sb)[2]) __attribute__((always_inline)) {
+      const bool next = t + 1 < t_wave_end;
+
+      // V^T operands of block C (tile t's stage); the first k-step's reads
+      // go out at the end of block A.
+      const uint32_t vb = lds_base + ((t - t_begin) & (kRingP - 1)) * G::kStageElems * 2 +
+                          G::kTileElems * 2 + v_off[0];
+      uint32_t vt[G::kOTiles];
+#pragma unroll
+      for (int t2 = 0; t2 < G::kOTiles; ++t2) vt[t2] = vb ^ (uint32_t)(t2 << 6);
+      u32x4 va[4][G::kOTiles];
+      auto vread = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+          const uint32_t a = vt[t2] + (16 * j) * D * 2;
+          const u32x2 a0 = lds_read_tr16(a), a1 = lds_read_tr16(a + 4 * D * 2);
+          va[j][t2] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        }
+      };
+
+      // ---------------- block A ----------------
+      const uint32_t kb = lds_base + ((t + 1 - t_begin) & (kRingP - 1)) * G::kStageElems * 2 +
+                          k_off[0];
+      u32x4 ka[G::kQSteps][2];
+      auto kread = [&](int ks) __attribute__((always_inline)) {
+        const uint32_t addr = kb ^ (uint32_t)(ks << 5);
+        ka[ks][0] = *(const lds_u32x4*)(uintptr_t)addr;
+        ka[ks][1] = *(const lds_u32x4*)(uintptr_t)(addr + 32 * D * 2);
+      };
+      float pe[32];
+      u32x4 pb[4];
+      float ps0 = 0.f, ps1 = 0.f;
+      // Vector work of block A in 16 slices: exponentials (slices 0-7),
+      // packs one slice behind them (2, 4, 6, 8), row sums (9-12).
+      auto valu_a = [&](int c) __attribute__((always_inline)) {
+        if (c < 8) {
+          const int j = c >> 1, h = c & 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pe[8 * j + 4 * h + e] = fast_exp2(sa[j >> 1][8 * (j & 1) + 4 * h + e]);
+        }
+        if (c >= 2 && c <= 8 && (c & 1) == 0) {
+          const int j = c / 2 - 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pb[j][e] = T::pack(pe[8 * j + 2 * e], pe[8 * j + 2 * e + 1]);
+        }
+        if (c >= 9 && c <= 12) {
+          const int j = c - 9;
+          ps0 = T::add_pair(pb[j][0], ps0);
+          ps1 = T::add_pair(pb[j][1], ps1);
+          ps0 = T::add_pair(pb[j][2], ps0);
+          ps1 = T::add_pair(pb[j][3], ps1);
+        }
+        if (c == 13) l_run[0] += ps0 + ps1;
+      };
+#pragma unroll
+      for (int ks = 0; ks < kKpf; ++ks) kread(ks);
+      sb[0] = sb[1] = f32x16{};
+      fence();
+#pragma unroll
+      for (int ks = 0; ks < G::kQSteps; ++ks) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int slot = 2 * ks + hh;
+          sb[hh] = T::mfma32x32x16(ka[ks][hh], qT[0][ks], sb[hh]);
+          if constexpr (kSlotsA == 16) {
+            valu_a(slot);
+          } else {
+            valu_a(2 * slot);
+            valu_a(2 * slot + 1);
+          }
+          if (hh == 1 && ks + kKpf < G::kQSteps) kread(ks + kKpf);
+          fence();
+        }
+      }
+      // The weights and l are formed here, beside the MFMAs: an empty use keeps
+      // the compiler from sinking them below the branch that follows.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(pb[j]));
+      asm volatile("" ::"v"(l_run[0]));
+      vread(0);
+      fence();
+
+      // Masked scores of tile t+1 (straddling the diagonal, the pad or the
+      // ends of the key range) become -inf: a rare branch.
+      const int j1 = (t + 1) * kBc;
+      const bool need_mask = next && ((CAUSAL && j1 + kBc - 1 > wq0 + qoff) ||
+                                      (j1 + kBc > key_hi) || (j1 < key_lo));
+      if (__builtin_expect(need_mask, 0)) mask(t + 1, sb);
+
+      // ---------------- block C ----------------
+      // Vector work of block C in 16 slices: the row max of tile t+1 over its
+      // two score tiles (slices 1-8, after the first MFMA so that block A's
+      // last MFMAs have finished), the running-max decision (9), and the exp2
+      // arguments (10-15).
+      float mp[2][3], mh[2];
+      float m_new = m_run[0];
+      const float raise_above = next ? m_run[0] + kSlack : __builtin_inff();
+      bool raise = false;
+      auto max3f = [](float x, float y, float z) { return fmaxf(fmaxf(x, y), z); };
+      auto valu_c = [&](int c) __attribute__((always_inline)) {
+        if (c >= 1 && c <= 8) {
+          const int mt = (c - 1) >> 2, k = (c - 1) & 3;
+          const f32x16& x = sb[mt];
+          if (k == 0) { mp[mt][0] = max3f(x[0], x[1], x[2]); mp[mt][1] = max3f(x[3], x[4], x[5]); }
+          if (k == 1) { mp[mt][2] = max3f(x[6], x[7], x[8]); mp[mt][0] = max3f(mp[mt][0], x[9], x[10]); }
+          if (k == 2) { mp[mt][1] = max3f(mp[mt][1], x[11], x[12]); mp[mt][2] = max3f(mp[mt][2], x[13], x[14]); }
+          if (k == 3) mh[mt] = fmaxf(max3f(mp[mt][0], mp[mt][1], mp[mt][2]), x[15]);
+        }
+        if (c == 9) {
+          const float mxc = max_xor32(fmaxf(mh[0], mh[1])) * c_scale;
+          raise = mxc > raise_above;  // never for the surplus tile
+          m_new = raise ? mxc : m_run[0];
+        }
+        if (c >= 10) {
+          const int i0 = (c - 10) * 32 / 6, i1 = (c - 9) * 32 / 6;
+#pragma unroll
+          for (int i = i0; i < i1; ++i) sb[i >> 4][i & 15] = fmaf(sb[i >> 4][i & 15], c_scale, -m_new);
+        }
+      };
+      vread(1);
+      fence();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+          const int slot = j * G::kOTiles + t2;
+          acc[t2][0] = T::mfma32x32x16(va[j][t2], pb[j], acc[t2][0]);
+          if constexpr (kSlotsC == 16) {
+            valu_c(slot);
+          } else {
+            valu_c(2 * slot);
+            valu_c(2 * slot + 1);
+          }
+          if (t2 == G::kOTiles - 1 && j + 2 < 4) vread(j + 2);
+          fence();
+        }
+      }
+      // The arguments are formed here, beside the MFMAs (see above).
+#pragma unroll
+      for (int i = 0; i < 32; ++i) asm volatile("" ::"v"(sb[i >> 4][i & 15]));
+      if (__builtin_expect(__any(raise), 0)) {
+        asm volatile("" ::: "memory");  // a real branch, not a speculated rescale
+        rescale(m_new);
+      }
+      m_run[0] = m_new;
+    };
+
+    f32x16 sa[2], sb[2];
+    // Prologue: tile t_begin's scores and arguments.
+    scores(t_begin, sa);
+    if (t_begin < t_wave_end) {
+      const int jb = t_begin * kBc;
+      const bool need_mask = (CAUSAL && jb + kBc - 1 > wq0 + qoff) || (jb + kBc > key_hi) ||
+                             (jb < key_lo);
+      if (need_mask) mask(t_begin, sa);
+      float m_new;
+      softmax_args(sa, true, m_new);
+      m_run[0] = m_new;  // acc and l are still zero: nothing to rescale
+    }
+    for (int t = t_begin; t < t_end; ++t) {
+      // This wave's DMAs of tile t+1 are done and its LDS reads are
+      // finished; after the barrier every wave may read tile t+1, and the
+      // stage of tile t-1 is free for tile t+3.
+      if (t + 2 < t_end) wait_vm_lgkm0<G::kDmaPerWave>();
+      else wait_vm_lgkm0<0>();
+      bare_barrier();
+      if (t + 3 < t_end) issue_tile(t + 3, (t + 3 - t_begin) & (kRingP - 1));
+      if (t < t_wave_end) {
+        step(t, sa, sb);
+        sa[0] = sb[0];
+        sa[1] = sb[1];
+      }
     }
   }
 

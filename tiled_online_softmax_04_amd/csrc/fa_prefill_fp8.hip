@@ -101,18 +101,6 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-// Transposing byte read: within each 16 lanes, lane 2r+t names row r, bytes
-// 8t..8t+7 of a 16-byte chunk; lane c receives byte c of that chunk from each
-// of the 8 rows (row r in byte r).  OFF lands in the instruction's offset
-// field; the result is valid after wait_lgkm0() and reg_barrier() on it.
-template <int OFF>
-__device__ __forceinline__ u32x2 ds_read_tr8_at(uint32_t lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF)
-               : "memory");
-  return r;
-}
-
 __device__ __forceinline__ u32x8 cat(u32x4 a, u32x4 b) {
   return u32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -162,8 +150,6 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
   // K and V of this head as buffers over exactly [key_lo, m): padding rows
   // and rows past the end read back as zeros.
   const uint32_t kv_bytes = (uint32_t)max(key_hi - key_lo, 0) * (uint32_t)D;
-  const __amdgpu_buffer_rsrc_t rsrc_k = make_rsrc(K + kv_base + (size_t)key_lo * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_v = make_rsrc(V + kv_base + (size_t)key_lo * D, kv_bytes);
 
   // DMA of a tile into a ring stage: lane l fills LDS row p = first + l /
   // kChunks, physical chunk l % kChunks, with the key (kappa order for K) and
@@ -179,17 +165,20 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     const int chunk = pc ^ (dma_v ? v_swz8<D>(p) : k_swz8<D>(p));
     dma_off[i] = (uint32_t)(key * D + chunk * 16);
   }
-  const __amdgpu_buffer_rsrc_t rsrc_dma = dma_v ? rsrc_v : rsrc_k;
+  const u32x4 rsrc_dma_words = make_rsrc_words(
+      (dma_v ? V : K) + kv_base + (size_t)key_lo * D, kv_bytes);
   lds_char* const lds = (lds_char*)smem;
   const int dma_lds0 = (dma_v ? G::kTileBytes : 0) +
                        (w * G::kDmaPerWave - (dma_v ? G::kDmaPerTile : 0)) * G::kRowsPerDma * D;
   auto issue_tile = [&](int t, int st) {
-    lds_char* dst = lds + st * G::kStageBytes + dma_lds0;
+    const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds + st * G::kStageBytes + dma_lds0));
     // (t * kBc8 - key_lo) may be negative: it wraps past 2^31 and reads zeros.
     const uint32_t tile_off = (uint32_t)((t * kBc8 - key_lo) * D);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i)
-      dma16(rsrc_dma, tile_off + dma_off[i], dst + i * G::kRowsPerDma * D);
+      dma16_untracked(rsrc_dma_words, tile_off + dma_off[i],
+                      dst + (uint32_t)(i * G::kRowsPerDma * D));
   };
 #pragma unroll
   for (int i = 0; i < (kGroup8 > 1 ? kGroup8 : kStages8 - 1); ++i)
@@ -268,9 +257,11 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
         constexpr int g = decltype(Gc)::value;
         constexpr int off = (32 * (g >> 1) + 16 * (g & 1)) * D;
 #pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) vr[g][t2] = ds_read_tr8_at<off>(vs_addr + v_off[t2]);
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) vr[g][t2] = lds_read_tr8(vs_addr + v_off[t2] + off);
       };
-      static_for<0, 2>([&](auto Gc) __attribute__((always_inline)) { issue_v(Gc); });
+      __builtin_amdgcn_sched_barrier(0);
+        static_for<0, 2>([&](auto Gc) __attribute__((always_inline)) { issue_v(Gc); });
+        __builtin_amdgcn_sched_barrier(0);  // the V^T reads go out here
 
       // Mask only tiles that straddle the diagonal, the pad or the end of K.
       const bool need_mask = (CAUSAL && j0 + kBc8 - 1 > wq0) || (j0 + kBc8 > key_hi) ||
@@ -321,12 +312,12 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
       }
       lacc = mfma_fp8(ones, pb, lacc);
 
-      static_for<2, 4>([&](auto Gc) __attribute__((always_inline)) { issue_v(Gc); });
+      __builtin_amdgcn_sched_barrier(0);
+        static_for<2, 4>([&](auto Gc) __attribute__((always_inline)) { issue_v(Gc); });
+        __builtin_amdgcn_sched_barrier(0);  // the V^T reads go out here
       wait_lgkm0();
 #pragma unroll
       for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) reg_barrier(vr[g][t2]);
         const u32x8 va = {vr[0][t2][0], vr[0][t2][1], vr[1][t2][0], vr[1][t2][1],
                           vr[2][t2][0], vr[2][t2][1], vr[3][t2][0], vr[3][t2][1]};
         acc[t2] = mfma_fp8(va, pb, acc[t2]);
