@@ -41,7 +41,10 @@ extern "C" {
 typedef enum {
   FA_DTYPE_F32 = 0,  /* float32 in and out; scores and the softmax shift in float64 */
   FA_DTYPE_F16 = 1,  /* float16 in and out; MFMA with float32 accumulation        */
-  FA_DTYPE_BF16 = 2  /* bfloat16 in and out; MFMA with float32 accumulation       */
+  FA_DTYPE_BF16 = 2, /* bfloat16 in and out; MFMA with float32 accumulation       */
+  /* Not a dtype.  It makes every int value a valid fa_dtype, so a caller that
+   * passes an unknown code gets FA_ERR_INVALID rather than undefined behaviour. */
+  FA_DTYPE_MAX_ENUM = 0x7fffffff
 } fa_dtype;
 
 typedef enum {
@@ -49,7 +52,8 @@ typedef enum {
   FA_ERR_INVALID = 1,      /* an argument breaks the contract (null, range, shape)   */
   FA_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement            */
   FA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required             */
-  FA_ERR_HIP = 4           /* the HIP runtime reported an error (see fa_last_error)  */
+  FA_ERR_HIP = 4,          /* the HIP runtime reported an error (see fa_last_error)  */
+  FA_STATUS_MAX_ENUM = 0x7fffffff  /* not a status: makes every int a valid fa_status  */
 } fa_status;
 
 /*

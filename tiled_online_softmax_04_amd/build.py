@@ -1,6 +1,7 @@
 """Builds libfa.so (the HIP kernels and their C ABI) for gfx950, in-tree.
 
     python -m tiled_online_softmax_04_amd.build
+    python -m tiled_online_softmax_04_amd.build --sanitized   # host code under ASan/UBSan
 """
 from __future__ import annotations
 
@@ -57,5 +58,50 @@ def build(verbose: bool = False) -> str:
     return OUT
 
 
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_OUT = os.path.join(SAN_DIR, "libfa_san.so")
+# Host code only: the device pass of a .hip file is never instrumented.
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (UBSan's handlers
+    are part of it); a process that loads the sanitized library preloads it."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError(f"no shared AddressSanitizer runtime found ({out!r})")
+    return out
+
+
+def build_sanitized() -> str:
+    """libfa.so with the C ABI layer (fa_api.hip: argument checks, dispatch and
+    error reporting) compiled with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host code; the kernel objects are those of build().  Written to
+    _build/san/libfa_san.so, never over the product library."""
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES[1:]]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    api_obj = os.path.join(SAN_DIR, "fa_api.o")
+    flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS
+    r = subprocess.run([HIPCC, *flags, "-c", os.path.join(CSRC, "fa_api.hip"), "-o", api_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized fa_api.hip:\n" + r.stdout + r.stderr)
+    # The sanitizer symbols stay undefined here; the preloaded runtime supplies them.
+    tmp = SAN_OUT + ".tmp"
+    subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, api_obj, *objs,
+                    "-Wl,-rpath,/opt/rocm/lib"], check=True)
+    os.replace(tmp, SAN_OUT)
+    return SAN_OUT
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitized" in sys.argv:
+        print(build_sanitized())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -40,6 +40,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "unsupported configuration";
     case FA_ERR_WORKSPACE: return "workspace too small";
     case FA_ERR_HIP: return "HIP runtime error";
+    default: break;
   }
   return "unknown status";
 }

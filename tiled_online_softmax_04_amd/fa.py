@@ -13,7 +13,9 @@ import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa.so")
+# FA_LIBRARY selects another build of the same library, such as the build of
+# the C ABI's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
