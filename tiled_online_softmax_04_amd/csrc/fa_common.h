@@ -162,6 +162,27 @@ __device__ __forceinline__ int xcd_by_group(int bid, int total, int per_group) {
   return (x + 8 * (k / per_group)) * per_group + k % per_group;
 }
 
+// Causal form of xcd_by_group.  The units are (group, head of the group,
+// Q-tile rank r); rank r = 0 is the heaviest (the last Q tile, which sees the
+// most keys).  XCD x still takes the groups x, x + 8, ..., in chunks of up to
+// four groups; within a chunk it hands out rank 0 of every unit first, then
+// rank 1, and so on, so each chunk ends on its lightest tiles and no heavy
+// tile starts last, while only a chunk's K/V (four groups) is live in the
+// XCD's L2 at a time.  Returns the logical id (group * heads + head) *
+// q_tiles + r, as xcd_by_group lays it out.
+__device__ __forceinline__ int xcd_heavy_first(int bid, int total, int per_group, int q_tiles) {
+  if ((total / per_group) % 8 != 0) return xcd_contiguous(bid, total);
+  const int x = bid % 8, k = bid / 8;
+  const int heads = per_group / q_tiles;  // query heads per group
+  const int gx = total / per_group / 8;   // groups of XCD x
+  const int cg = gx % 4 == 0 ? 4 : gx % 2 == 0 ? 2 : 1;  // groups per chunk
+  const int per_chunk = cg * per_group;
+  const int c = k / per_chunk, kk = k % per_chunk;
+  const int r = kk / (cg * heads), j = kk % (cg * heads);
+  const int gi = c * cg + j / heads, hg = j % heads;
+  return ((x + 8 * gi) * heads + hg) * q_tiles + r;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I in [B, E).
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
   // Work units are (batch, query head, Q tile), Q tiles fastest; the units of
   // one KV group (batch, KV head) are consecutive.
-  const int logical = xcd_by_group(blockIdx.x, total, group * q_tiles);
+  const int logical = CAUSAL ? xcd_heavy_first(blockIdx.x, total, group * q_tiles, q_tiles)
+                             : xcd_by_group(blockIdx.x, total, group * q_tiles);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   // Causal tiles further down hold more keys: hand those out first.
