@@ -163,6 +163,7 @@ def dec(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, d=128, 
     (dict(scale=0.0), fa.FA_ERR_INVALID),
     (dict(d=80, dv=80), fa.FA_ERR_UNSUPPORTED),
     (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(maxb=1 << 26), fa.FA_ERR_UNSUPPORTED),  # 2^30 keys: over 65535 splits
     (dict(bt=None), fa.FA_ERR_INVALID),
     (dict(sl=None), fa.FA_ERR_INVALID),
     (dict(kc=MISALIGNED), fa.FA_ERR_INVALID),

@@ -275,6 +275,11 @@ static fa_status check_decode(fa_dtype dt, const void* q, const void* k_cache,
     return fail(FA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
   const fa::DecodePlan p =
       fa::decode_plan(num_seqs, heads_q, heads_kv, max_blocks_per_seq, block_size);
+  if (p.max_splits > 65535)
+    return fail(FA_ERR_UNSUPPORTED,
+                "max_blocks_per_seq * block_size = %lld keys need %d splits of %d, above the "
+                "65535 a launch grid holds",
+                (long long)max_blocks_per_seq * block_size, p.max_splits, p.split_tokens);
   *need = fa::decode_workspace_bytes(p, num_seqs, heads_q, dv);
   return FA_OK;
 }

@@ -123,7 +123,8 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
 
   // Units (batch, query head, Q tile), Q tiles fastest; KV groups dealt to
   // the XCDs in turn.
-  const int logical = xcd_by_group(blockIdx.x, total, group * q_tiles);
+  const int logical = CAUSAL ? xcd_heavy_first(blockIdx.x, total, group * q_tiles, q_tiles)
+                             : xcd_by_group(blockIdx.x, total, group * q_tiles);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   const int qt = CAUSAL ? q_tiles - 1 - qt_ord : qt_ord;  // longest causal rows first
