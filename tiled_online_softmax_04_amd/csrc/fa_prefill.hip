@@ -55,9 +55,10 @@ constexpr int kThreads = 64 * kWaves;
 // LDS ring of K/V tiles: tile t is computed while tiles t+1 .. t+kStages-1 land.
 constexpr int kStages = FA_PREFILL_STAGES;
 static_assert(kStages == 2 || kStages == 3, "ring depth");
-// LDS stages of the K/V ring: three for the paged form (one tile per barrier,
-// two tiles ahead), four for the contiguous form's pipeline.
-constexpr int ring_stages(bool paged) { return paged ? kStages : 4; }
+// LDS stages of the K/V ring: four for the software pipeline (contiguous K/V,
+// and paged K/V whose block table fits beside the ring), three for the paged
+// form with a large block table (one tile per barrier, two tiles ahead).
+constexpr int ring_stages(bool tile_loop) { return tile_loop ? kStages : 4; }
 
 template <int D>
 struct Geo {
@@ -91,10 +92,14 @@ __device__ __forceinline__ int v_swz(int row) {
 // PARTIAL: attend only to keys in [key_begin, key_end) and write the result
 // normalised over that range as float32 (Of) together with the natural-log
 // softmax denominator of the range (Lse), instead of the final O.
-// PAGED: K and V are paged caches [num_blocks, bs, Hkv, D] reached through
-// block_table; the n query rows of sequence b are its last n tokens (row i is
-// token seq_lens[b] - n + i) and the causal mask is aligned to that.
-template <class T, int D, bool CAUSAL, bool RAGGED, bool PARTIAL, bool PAGED>
+// PG (paged): 0 for contiguous K and V.  Otherwise K and V are paged caches
+// [num_blocks, bs, Hkv, D] reached through block_table; the n query rows of
+// sequence b are its last n tokens (row i is token seq_lens[b] - n + i) and
+// the causal mask is aligned to that.  PG = 1 runs the software-pipelined key
+// loop (block table of up to kMaxPipelinedPagedBlocks entries, staged in LDS
+// beside the four-stage ring), PG = 2 the one-tile-per-barrier loop over a
+// three-stage ring for tables of up to kMaxPagedBlocks entries.
+template <class T, int D, bool CAUSAL, bool RAGGED, bool PARTIAL, int PG>
 #ifndef FA_PREFILL_WAVES_PER_EU
 #define FA_PREFILL_WAVES_PER_EU (kWaves / 4)
 #endif
@@ -105,7 +110,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     int m, int key_begin, int key_end, int q_tiles, int total, float c,
     const int32_t* __restrict__ block_table, int bs, int bs_shift, int maxb, int num_blocks) {
   using G = Geo<D>;
-  constexpr int kRing = ring_stages(PAGED);
+  constexpr bool PAGED = PG != 0;
+  constexpr int kRing = ring_stages(PG == 2);
   extern __shared__ __align__(16) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     }
   };
 
-  if constexpr (PAGED) {
+  if constexpr (PG == 2) {
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i)
       if (t_begin + i < t_end) issue_tile(t_begin + i, i);
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       v_off[t2] = (uint32_t)(key * D + (((4 * t2 + chunk) ^ v_swz<D>(key)) * 8) + (i & 1) * 4) * 2u;
   }
 
-  if constexpr (PAGED) {
+  if constexpr (PG == 2) {
     wait_vm_lgkm0<0>();
     bare_barrier();
 
@@ -440,9 +446,9 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     }
   } else {
     // ---------------------------------------------------------------------
-    // Contiguous K/V: a software pipeline over key tiles, one barrier per
-    // tile, four LDS stages (tiles t and t+1 in use, t+2 landing, t+3 being
-    // issued).  Each step issues the S^T MFMAs of tile t+1 beside tile t's
+    // Contiguous K/V, or paged K/V with a small block table: a software
+    // pipeline over key tiles, one barrier per tile, four LDS stages (tiles t
+    // and t+1 in use, t+2 landing, t+3 being issued).  Each step issues the S^T MFMAs of tile t+1 beside tile t's
     // exponentials, packing and row sums, then tile t's P.V MFMAs beside
     // tile t+1's row max, running-max update and exp2 arguments, so that a
     // wave's vector work sits between its own MFMAs (measured on gfx950: a
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     // ---------------------------------------------------------------------
     static_assert(kNT == 1, "the pipelined loop takes 32 queries per wave");
     constexpr int kRingP = 4;
-    static_assert(ring_stages(false) == kRingP, "LDS ring of the pipelined loop");
+    static_assert(kRing == kRingP, "LDS ring of the pipelined loop");
     // Tiles this wave computes: [t_begin, t_wave_end).  Later tiles lie wholly
     // above its causal diagonal; a wave of padding rows or rows past n
     // computes none.  It still moves its share of every tile and meets every
@@ -461,6 +467,8 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     if constexpr (CAUSAL) t_wave_end = min(t_wave_end, (wq0 + qoff + kQPerWave - 1) / kBc + 1);
     if constexpr (RAGGED)
       if (wq0 + kQPerWave - 1 < pad) t_wave_end = t_begin;
+    if constexpr (PAGED)  // rows before the sequence's first token
+      if (wq0 + qoff + kQPerWave - 1 < 0) t_wave_end = t_begin;
     t_wave_end = __builtin_amdgcn_readfirstlane(max(t_wave_end, t_begin));
 
     // The query loads above go out before the first tiles.
@@ -903,20 +911,24 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// Largest block table a paged launch stages in LDS (after the K/V ring).
+// Largest block table a paged launch stages in LDS after the K/V ring: with
+// the three-stage ring, and with the pipelined loop's four-stage ring (both
+// fill the 160 KB of LDS at d = 128).
 constexpr int kMaxPagedBlocks = 16384;
+constexpr int kMaxPipelinedPagedBlocks = 8192;
 
-template <class T, int D, bool C, bool R, bool P, bool PG>
+template <class T, int D, bool C, bool R, bool P, int PG>
 static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
   const int q_tiles = (a.n + kBr - 1) / kBr;
   const long long total = (long long)a.batch * a.heads_q * q_tiles;
-  const size_t ring = ring_stages(PG) * G::kStageElems * sizeof(uint16_t);
+  const size_t ring = ring_stages(PG == 2) * G::kStageElems * sizeof(uint16_t);
   const size_t lds = PG ? ring + (size_t)a.max_blocks * sizeof(int32_t) : ring;
+  const int table_max = PG == 1 ? kMaxPipelinedPagedBlocks : kMaxPagedBlocks;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&fa_fwd_mfma<T, D, C, R, P, PG>),
       hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(PG ? ring + kMaxPagedBlocks * sizeof(int32_t) : ring));
+      (int)(PG ? ring + table_max * sizeof(int32_t) : ring));
   if (attr != hipSuccess) return attr;
   const int bs = PG ? a.block_size : 1;
   const int shift = (PG && (bs & (bs - 1)) == 0) ? __builtin_ctz((unsigned)bs) : -1;
@@ -943,15 +955,19 @@ static hipError_t launch_f32(const FwdArgs& a) {
 
 template <class T, int D, bool P>
 static hipError_t dispatch_mask(const FwdArgs& a) {
-  if (a.paged)  // paged chunks: no left padding, full key range
-    return a.causal ? launch_mfma<T, D, true, false, false, true>(a)
-                    : launch_mfma<T, D, false, false, false, true>(a);
+  if (a.paged) {  // paged chunks: no left padding, full key range
+    if (a.max_blocks <= kMaxPipelinedPagedBlocks)
+      return a.causal ? launch_mfma<T, D, true, false, false, 1>(a)
+                      : launch_mfma<T, D, false, false, false, 1>(a);
+    return a.causal ? launch_mfma<T, D, true, false, false, 2>(a)
+                    : launch_mfma<T, D, false, false, false, 2>(a);
+  }
   const bool r = a.seq_lens != nullptr;
   if (a.causal)
-    return r ? launch_mfma<T, D, true, true, P, false>(a)
-             : launch_mfma<T, D, true, false, P, false>(a);
-  return r ? launch_mfma<T, D, false, true, P, false>(a)
-           : launch_mfma<T, D, false, false, P, false>(a);
+    return r ? launch_mfma<T, D, true, true, P, 0>(a)
+             : launch_mfma<T, D, true, false, P, 0>(a);
+  return r ? launch_mfma<T, D, false, true, P, 0>(a)
+           : launch_mfma<T, D, false, false, P, 0>(a);
 }
 
 template <int D, bool P>
