@@ -9,13 +9,14 @@
 // v_mfma_f32_32x32x16, applies the online-softmax update of the same section
 // (running max, rescale of the history by exp(m_old - m_new), running sum) and
 // accumulates O^T += V^T P^T with a second MFMA whose V^T operands come from
-// transposing LDS reads.  Contiguous K/V run as a software pipeline over the
-// tiles (one barrier per tile, four stages): tile t+1's scores are formed
-// beside tile t's exponentials, and tile t's P.V beside tile t+1's row max.
-// The paged form keeps one tile per barrier, three stages, two tiles ahead,
-// with the softmax between the two products.  Tiles wholly above the causal
-// diagonal or wholly inside a left pad are never visited (10100.com
-// section 6).
+// transposing LDS reads.  The key loop is a software pipeline over the tiles
+// (one barrier per tile, four stages): tile t+1's scores are formed beside
+// tile t's exponentials, and tile t's P.V beside tile t+1's row max.  This
+// holds for contiguous K/V and for paged K/V whose block table fits in LDS
+// after the ring; a larger table takes a loop of one tile per barrier over
+// three stages, two tiles ahead, with the softmax between the two products.
+// Tiles wholly above the causal diagonal or wholly inside a left pad are never
+// visited (10100.com section 6).
 //
 // Why S^T rather than S: in the 32x32 MFMA accumulator each lane holds one
 // column and 16 rows.  With keys as rows and queries as columns every lane
