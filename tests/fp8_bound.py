@@ -75,6 +75,40 @@ def row_bounds(q_rows, row_idx, k, v, scale, causal=False, pad=0):
     return O, B, sig
 
 
+def row_bounds_fast(q_rows, row_idx, k, v, scale, causal=False, pad=0):
+    """row_bounds in matrix products only, for whole outputs.  The rms
+    estimate is the same: sum_j e_j^2 (v_j - O)^2 expands into
+    (e^2) v^2 - 2 O (e^2) v + O^2 sum e^2.  The rigorous bound takes
+    sum_j e_j |v_j - O| <= sqrt(sum_j e_j) sqrt(sum_j e_j (v_j - O)^2)
+    (Cauchy-Schwarz, e_j >= 0) in place of the per-row sum, so it is never
+    tighter than row_bounds' and still holds wherever that one does."""
+    row_idx = np.asarray(row_idx, dtype=np.int64).reshape(-1)
+    key_idx = np.arange(k.shape[0], dtype=np.int64)
+    ok = oracle.allowed_keys(row_idx, key_idx, causal, pad)
+    P = oracle.masked_softmax(oracle.scores(q_rows, k, scale), ok)
+    O = P @ v
+    top = P.max(axis=1, keepdims=True)
+    has = top[:, 0] > 0
+    pm = P / np.where(top > 0, top, 1.0)
+    ds = MFMA_REL * scale * (np.abs(q_rows) @ np.abs(k).T)
+    grow = np.exp(ds)
+    sub = (pm / grow < SUB_P) & ok
+    e = pm * (grow * (1.0 + REL_P) - 1.0) + np.where(sub, np.minimum(ABS_P, pm * grow), 0.0)
+    den = pm.sum(axis=1) - e.sum(axis=1)
+    assert np.all(den[has] > 0), "bound undefined: rounding could cancel a row's weights"
+    den = np.where(has, den, 1.0)[:, None]
+    v2 = v * v
+
+    def dev2(w):  # sum_j w_j (v_j - O)^2, per row and column
+        return np.maximum(w @ v2 - 2.0 * O * (w @ v) + O * O * w.sum(axis=1, keepdims=True), 0.0)
+
+    num = np.sqrt(e.sum(axis=1, keepdims=True) * dev2(e)) + MFMA_REL * ((pm + e) @ np.abs(v))
+    B = np.where(has[:, None], num / den + OUT_REL * np.abs(O), 0.0)
+    sig = np.sqrt(dev2(e * e)) / den
+    sig = np.where(has[:, None], np.sqrt(sig ** 2 + (2.0 ** -9 * O) ** 2), 0.0)
+    return O, B, sig
+
+
 def head_bounds(q, k, v, scale, causal=False, pad=0, chunk=128):
     """row_bounds over all rows of one head (rows before pad get zeros)."""
     n = q.shape[0]

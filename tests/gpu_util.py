@@ -45,3 +45,42 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, label: str = "")
     assert bad == 0, f"{label}: {bad} non-finite outputs"
     assert mx <= tmax, f"{label}: max abs {mx:.3e} > {tmax}"
     assert mean <= tmean, f"{label}: mean abs {mean:.3e} > {tmean}"
+
+
+def host_workers() -> int:
+    """Worker threads for the oracle: this process's cores, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def pooled(fn, items):
+    """fn over items on a thread pool, BLAS single-threaded in each worker
+    (the oracle's matmuls per head are small; the heads run side by side)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"):
+        with ThreadPoolExecutor(host_workers()) as pool:
+            return list(pool.map(fn, items))
+
+
+def error_sums(got: np.ndarray, ref: np.ndarray):
+    """(max abs error, sum of abs errors, non-finite count, element count)."""
+    bad = int((~np.isfinite(got)).sum())
+    diff = np.abs(np.where(np.isfinite(got), got, 0.0) - ref)
+    return float(diff.max(initial=0.0)), float(diff.sum()), bad, int(diff.size)
+
+
+def assert_whole(parts, dtype: str, label: str, tol=None):
+    """Combines error_sums over the parts of a whole output and applies the
+    bar (or tol = (max, mean)) to the whole: max abs, mean abs over every
+    element, no non-finite value."""
+    mx = max(p[0] for p in parts)
+    total = sum(p[1] for p in parts)
+    bad = sum(p[2] for p in parts)
+    count = sum(p[3] for p in parts)
+    mean = total / max(count, 1)
+    tmax, tmean = TOL[dtype] if tol is None else tol
+    say(f"  {label} (all {count} outputs): max_abs={mx:.3e} mean_abs={mean:.3e} nonfinite={bad}")
+    assert bad == 0, f"{label}: {bad} non-finite outputs"
+    assert mx <= tmax, f"{label}: max abs {mx:.3e} > {tmax}"
+    assert mean <= tmean, f"{label}: mean abs {mean:.3e} > {tmean}"

@@ -63,3 +63,35 @@ def test_model_inside_bound(name, causal, hot, lens):
     # model leaves out)
     if hot == 1.0:
         assert max(ratios) > 0.1
+
+
+@pytest.mark.parametrize("name,causal,hot,lens", [
+    ("noncausal", False, 1.0, None),
+    ("causal_hot", True, 10.0, None),
+    ("causal_leftpad", True, 1.0, [150, 61]),
+])
+def test_fast_bound_against_exact(name, causal, hot, lens):
+    """row_bounds_fast (matrix products, for whole outputs) against row_bounds:
+    the same oracle output and rms estimate, and a rigorous bound at least as
+    large everywhere (Cauchy-Schwarz) that the CPU model of the path still
+    meets."""
+    x = gen.make_prefill_custom("fp8", 2, 1, 1, 150, 150, 64, 64, seed=11, hot=hot, lens=lens)
+    scale = float(np.float32(1 / 8.0))
+    for b in range(2):
+        pad = 0 if x["pads"] is None else int(x["pads"][b])
+        q = oracle.dequantize(x["q"][b, 0], x["q_descale"])
+        k = oracle.dequantize(x["k"][b, 0], x["k_descale"])
+        v = oracle.dequantize(x["v"][b, 0], x["v_descale"])
+        rows = np.arange(pad, 150)
+        o1, b1, s1 = fp8_bound.row_bounds(q[pad:], rows - pad, k[pad:], v[pad:], scale, causal)
+        o2, b2, s2 = fp8_bound.row_bounds_fast(q[pad:], rows - pad, k[pad:], v[pad:], scale,
+                                               causal)
+        assert np.allclose(o1, o2, rtol=0, atol=1e-12)
+        assert np.allclose(s1, s2, rtol=1e-9, atol=1e-15)
+        assert np.all(b2 >= b1 * (1 - 1e-12))
+        # looser, not vacuous: about 1.24x on average (elements of hot causal
+        # rows, where the exact per-key sum nearly cancels, reach some 100x)
+        assert b2.mean() <= 2.0 * b1.mean()
+        got = model_head(x["q"][b, 0], x["k"][b, 0], x["v"][b, 0], x["q_descale"],
+                         x["k_descale"], x["v_descale"], scale, causal, pad)[pad:]
+        fp8_bound.check(got, o2, b2, s2, f"{name} b={b} (fast bound)")

@@ -12,7 +12,7 @@ import oracle
 from tiled_online_softmax_04_amd import fa
 from tiled_online_softmax_04_amd import inputs as gen
 
-from gpu_util import assert_parity, say, to_dev, to_f64
+from gpu_util import assert_parity, host_workers, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -133,12 +133,6 @@ def test_prefill_deterministic():
 # --------------------------------------------------------------------------
 # full workload sizes: every output element against the oracle
 # --------------------------------------------------------------------------
-def host_workers() -> int:
-    """Worker threads for the oracle: this process's cores, at most 16."""
-    import os
-    return max(1, min(16, len(os.sched_getaffinity(0))))
-
-
 def whole_output_errors(x, w, got_bits):
     """Max abs error, sum of abs errors and non-finite count of every output
     element of a full-size prefill workload against the oracle.  The oracle
