@@ -118,6 +118,47 @@ def test_fp8_constant_values():
     assert np.all(err <= 2.0 ** -20 * want)
 
 
+def whole_output_bound(x, w, got_bits, causal):
+    """Every output of a full-size FP8 workload (bf16 out, got_bits its
+    storage bits) against fp8_bound.row_bounds_fast, one (batch, head) at a
+    time in chunks of 512 rows (causal chunks see only the keys up to their
+    last row).  Returns (worst err / bound, rms error, rms spread, non-finite
+    count) over the whole output."""
+    g = w.Hq // w.Hkv
+
+    def one(bh):
+        b, h = bh
+        q = oracle.dequantize(x["q"][b, h], x["q_descale"])
+        k = oracle.dequantize(x["k"][b, h // g], x["k_descale"])
+        v = oracle.dequantize(x["v"][b, h // g], x["v_descale"])
+        got = gen.bf16_bits_to_f64(got_bits[b, h])
+        worst, err2, sig2, bad = 0.0, 0.0, 0.0, int((~np.isfinite(got)).sum())
+        for r0 in range(0, w.n, 512):
+            rows = np.arange(r0, min(w.n, r0 + 512))
+            hi = int(rows[-1]) + 1 if causal else k.shape[0]
+            ref, B, sig = fp8_bound.row_bounds_fast(q[rows], rows, k[:hi], v[:hi], w.scale,
+                                                    causal)
+            err = np.abs(got[rows] - ref)
+            worst = max(worst, float(np.max(np.where(B > 0, err / np.where(B > 0, B, 1.0),
+                                                     np.where(err > 0, np.inf, 0.0)))))
+            err2 += float(np.sum(err ** 2))
+            sig2 += float(np.sum(sig ** 2))
+        return worst, err2, sig2, bad
+
+    res = pooled(one, [(b, h) for b in range(w.B) for h in range(w.Hq)])
+    return (max(r[0] for r in res), (sum(r[1] for r in res) / got_bits.size) ** 0.5,
+            (sum(r[2] for r in res) / got_bits.size) ** 0.5, sum(r[3] for r in res))
+
+
+def assert_whole_bound(x, w, got_bits, causal, label):
+    worst, rms, rms_sig, bad = whole_output_bound(x, w, got_bits, causal)
+    say(f"  {label} (all {got_bits.size} outputs): worst err/bound={worst:.3f} "
+        f"rms={rms:.3e} rms_sigma={rms_sig:.3e} nonfinite={bad}")
+    assert bad == 0
+    assert worst <= 1.0, f"{label}: error above the FP8 bound (worst ratio {worst:.3f})"
+    assert rms <= 2.0 * rms_sig
+
+
 def test_fp8_full_size_whole_output():
     """The 2048-token bf16 workload stored as FP8, in the launch the benchmark
     times: every output element within the bound in matrix-product form
@@ -132,35 +173,7 @@ def test_fp8_full_size_whole_output():
     o = fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"], scale=w.scale)
     torch.cuda.synchronize()
     got_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
-    g = w.Hq // w.Hkv
-
-    def one(bh):
-        b, h = bh
-        q = oracle.dequantize(x["q"][b, h], x["q_descale"])
-        k = oracle.dequantize(x["k"][b, h // g], x["k_descale"])
-        v = oracle.dequantize(x["v"][b, h // g], x["v_descale"])
-        got = gen.bf16_bits_to_f64(got_bits[b, h])
-        worst, err2, sig2, bad = 0.0, 0.0, 0.0, int((~np.isfinite(got)).sum())
-        for r0 in range(0, w.n, 512):
-            rows = np.arange(r0, min(w.n, r0 + 512))
-            ref, B, sig = fp8_bound.row_bounds_fast(q[rows], rows, k, v, w.scale)
-            err = np.abs(got[rows] - ref)
-            worst = max(worst, float(np.max(np.where(B > 0, err / np.where(B > 0, B, 1.0),
-                                                     np.where(err > 0, np.inf, 0.0)))))
-            err2 += float(np.sum(err ** 2))
-            sig2 += float(np.sum(sig ** 2))
-        return worst, err2, sig2, bad
-
-    res = pooled(one, [(b, h) for b in range(w.B) for h in range(w.Hq)])
-    worst = max(r[0] for r in res)
-    rms = (sum(r[1] for r in res) / got_bits.size) ** 0.5
-    rms_sig = (sum(r[2] for r in res) / got_bits.size) ** 0.5
-    bad = sum(r[3] for r in res)
-    say(f"  cfg2_fp8 (all {got_bits.size} outputs): worst err/bound={worst:.3f} "
-        f"rms={rms:.3e} rms_sigma={rms_sig:.3e} nonfinite={bad}")
-    assert bad == 0
-    assert worst <= 1.0, f"error above the FP8 bound (worst ratio {worst:.3f})"
-    assert rms <= 2.0 * rms_sig
+    assert_whole_bound(x, w, got_bits, False, "cfg2_fp8")
     rng = np.random.default_rng(13)
     samples = [(0, 0), (w.B - 1, w.Hq - 1)] + \
         [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(6)]
@@ -175,15 +188,16 @@ def test_fp8_full_size_whole_output():
         fp8_bound.check(got, ref, B_, sig, f"cfg2_fp8 b={b} h={h} rows={rows.tolist()}", say)
 
 
-def test_fp8_causal_8k_sampled_and_deterministic():
-    """The causal 8192-token shape (32 heads) stored as FP8: sampled rows from
-    the first, the last and the tile-boundary positions within the bound, the
-    first row equal to V's first row up to the output rounding, and two calls
-    bitwise equal."""
+def test_fp8_causal_8k_whole_output_and_deterministic():
+    """The causal 8192-token shape (32 heads) stored as FP8: every output
+    within the bound in matrix-product form and the whole output's rms within
+    twice the spread; sampled rows from the first, the last and the
+    tile-boundary positions within the per-row bound, the first row equal to
+    V's first row up to the output rounding, and two calls bitwise equal."""
     import dataclasses
     import torch
     w = dataclasses.replace(gen.WORKLOADS["cfg3"], dtype="fp8", name="cfg3_fp8")
-    say("[fp8] causal 8192 x 32 heads, sampled rows")
+    say("[fp8] causal 8192 x 32 heads")
     x = gen.make_prefill(w)
     q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
     args = (q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"])
@@ -192,6 +206,8 @@ def test_fp8_causal_8k_sampled_and_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "not deterministic"
     assert bool(torch.isfinite(o.float()).all())
+    assert_whole_bound(x, w, o.view(torch.int16).cpu().numpy().view(np.uint16), True,
+                       "cfg3_fp8 causal 8192")
     rng = np.random.default_rng(17)
     for h in (0, 13, w.Hq - 1):
         rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 4095, w.n - 1],
