@@ -7,9 +7,15 @@
 //
 // Shape: one workgroup of 8 waves (two per SIMD) owns 256 query rows of one
 // (batch, head); each wave keeps its 32 query rows in VGPRs for the whole key
-// loop.  64-key K/V tiles stream through a four-stage LDS ring filled by
-// buffer loads that write LDS directly: two tiles are computed between
-// barriers while the next two land.
+// loop.  64-key K/V tiles stream through an LDS ring filled by buffer loads
+// that write LDS directly, two tiles (or pipeline steps) per barrier.  At
+// d = 128 the key loop is a software pipeline, as in the 16-bit kernel: each
+// step issues the next tile's score MFMAs beside this tile's exponentials and
+// E4M3 packing, then this tile's P.V MFMAs beside the next tile's row max and
+// exp2 arguments (five stages: the tiles of both steps and the one whose
+// scores the second step forms, while the next two land).  At d = 64 a step
+// would hold half as many MFMAs for the same vector work, and whole tiles are
+// computed in turn from one half of a four-stage ring while the other lands.
 // Both products run on v_mfma_f32_32x32x64_f8f6f4 (64 fp8 products per lane
 // per instruction, twice the bf16 rate):
 //   S^T = K Q^T: per 32-key block, d/64 MFMAs; K rows come from LDS (32
@@ -40,14 +46,19 @@ constexpr int kW8 = 8;           // waves per workgroup
 constexpr int kT8 = 64 * kW8;    // threads per workgroup
 constexpr int kBr8 = 32 * kW8;   // query rows per workgroup
 constexpr int kBc8 = 64;         // keys per tile
-constexpr int kStages8 = 3;      // LDS ring depth
-// Tiles computed between two barriers.  Two halve the barrier waits per
-// tile; the ring then holds four stages, two computed while two land.
-#ifndef FA8_GROUP
-#define FA8_GROUP 2
-#endif
-constexpr int kGroup8 = FA8_GROUP;
-constexpr int kRing8 = kGroup8 > 1 ? 2 * kGroup8 : kStages8;
+constexpr int kGroup8 = 2;       // tiles (or pipeline steps) between two barriers
+// d = 128 runs the software-pipelined key loop: at a barrier tiles t, t+1,
+// t+2 are in the ring (the second step forms the scores of t+2) while t+3,
+// t+4 land, five stages.  d = 64 computes two whole tiles between barriers
+// from one half of a four-stage ring while the next two land.
+template <int D>
+constexpr bool pipelined8() {
+  return D == 128;
+}
+template <int D>
+constexpr int ring8() {
+  return pipelined8<D>() ? 2 * kGroup8 + 1 : 2 * kGroup8;
+}
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(8 * sizeof(uint32_t)))) uint32_t u32x8;
@@ -114,6 +125,8 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     void* __restrict__ O, const int32_t* __restrict__ seq_lens, int Hq, int group, int n, int m,
     int q_tiles, int total, float c, float v_descale) {
   using G = Geo8<D>;
+  constexpr bool kPipe = pipelined8<D>();
+  constexpr int kRing8 = ring8<D>();
   __shared__ __align__(16) uint8_t smem[kRing8 * G::kStageBytes];
 
   const int tid = threadIdx.x;
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
                       dst + (uint32_t)(i * G::kRowsPerDma * D));
   };
 #pragma unroll
-  for (int i = 0; i < (kGroup8 > 1 ? kGroup8 : kStages8 - 1); ++i)
+  for (int i = 0; i < (kPipe ? kGroup8 + 1 : kGroup8); ++i)
     if (t_begin + i < t_end) issue_tile(t_begin + i, i);
 
   // Queries as B operands of S^T = K Q^T: lane holds query ql, 32 consecutive
@@ -221,6 +234,7 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
   wait_vm_lgkm0<0>();
   bare_barrier();
 
+  const float c_scale = c;
   // A whole wave above the causal diagonal, or wholly padding, skips a tile.
   auto wave_idle = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * kBc8;
@@ -334,36 +348,239 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     }
   };
 
-#if FA8_GROUP > 1
-  // kGroup8 tiles between barriers: they are computed from half of the ring
-  // while the next kGroup8 land in the other half.
-  for (int t = t_begin; t < t_end; t += kGroup8) {
-    const int it = t - t_begin;
+  if constexpr (!kPipe) {
+    // kGroup8 tiles between barriers: they are computed from half of the
+    // ring while the next kGroup8 land in the other half.
+    for (int t = t_begin; t < t_end; t += kGroup8) {
+      const int it = t - t_begin;
 #pragma unroll
-    for (int g = 0; g < kGroup8; ++g)
-      if (t + kGroup8 + g < t_end) issue_tile(t + kGroup8 + g, (it + kGroup8 + g) % kRing8);
+      for (int g = 0; g < kGroup8; ++g)
+        if (t + kGroup8 + g < t_end) issue_tile(t + kGroup8 + g, (it + kGroup8 + g) % kRing8);
 #pragma unroll
-    for (int g = 0; g < kGroup8; ++g)
-      if (t + g < t_end) tile(t + g, (it + g) % kRing8);
-    wait_vm_lgkm0<0>();
-    bare_barrier();
-  }
-#else
-  for (int t = t_begin; t < t_end; ++t) {
-    const int it = t - t_begin;
-    const bool pre = t + kStages8 - 1 < t_end;
-    if (pre) issue_tile(t + kStages8 - 1, (it + kStages8 - 1) % kStages8);
-    tile(t, it % kStages8);
-    // This wave's part of tile t+1 has landed and its reads of stage st are
-    // done; after the barrier every wave may read t+1 and refill stage st.
-    if (pre) {
-      wait_vm_lgkm0<(kStages8 - 2) * G::kDmaPerWave>();
-    } else {
+      for (int g = 0; g < kGroup8; ++g)
+        if (t + g < t_end) tile(t + g, (it + g) % kRing8);
       wait_vm_lgkm0<0>();
+      bare_barrier();
     }
-    bare_barrier();
+  } else {
+    // Software pipeline over the key tiles, kGroup8 steps between barriers.
+    // At a barrier tiles t .. t+kGroup8 are in the ring (the last step forms
+    // the scores of tile t+kGroup8), and tiles t+kGroup8+1 .. t+2 kGroup8 go
+    // into the stages that the steps before the barrier finished with.
+    int t_wave_end = t_end;  // tiles this wave computes: [t_begin, t_wave_end)
+    if (wq0 >= n) t_wave_end = t_begin;
+    if constexpr (CAUSAL) t_wave_end = min(t_wave_end, (wq0 + 31) / kBc8 + 1);
+    if constexpr (RAGGED)
+      if (wq0 + 31 < pad) t_wave_end = t_begin;
+    t_wave_end = __builtin_amdgcn_readfirstlane(max(t_wave_end, t_begin));
+    auto ring = [](int x) __attribute__((always_inline)) { return x >= kRing8 ? x - kRing8 : x; };
+
+    // Masked scores of a tile that straddles the diagonal, the pad or the
+    // end of K become -inf.
+    auto needs_mask = [&](int t) __attribute__((always_inline)) {
+      const int j0 = t * kBc8;
+      return (CAUSAL && j0 + kBc8 - 1 > wq0) || (j0 + kBc8 > key_hi) || (j0 < key_lo);
+    };
+    auto mask = [&](int t, f32x16 (&sc)[2]) __attribute__((always_inline)) {
+      const int j0 = t * kBc8;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 16 * (i >> 3) + 8 * hf + (i & 7);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int key = j0 + 32 * mt + kk;
+          const bool bad = key >= key_hi || key < key_lo || (CAUSAL && key > qrow);
+          sc[mt][i] = bad ? -__builtin_inff() : sc[mt][i];
+        }
+      }
+    };
+    // Row max of one 32-key block: this lane's 16 scores in max3 steps.
+    auto max16 = [](const f32x16& x) __attribute__((always_inline)) {
+      float a = fmaxf(fmaxf(x[0], x[1]), x[2]);
+      float b = fmaxf(fmaxf(x[3], x[4]), x[5]);
+      float d = fmaxf(fmaxf(x[6], x[7]), x[8]);
+      a = fmaxf(fmaxf(a, x[9]), x[10]);
+      b = fmaxf(fmaxf(b, x[11]), x[12]);
+      d = fmaxf(fmaxf(d, x[13]), x[14]);
+      return fmaxf(fmaxf(fmaxf(a, b), d), x[15]);
+    };
+
+    // One step of the pipeline.  On entry sa holds tile t's exp2 arguments
+    // s * c - m (formed in the step before, or the prologue).
+    //  block A: tile t+1's S^T MFMAs beside tile t's weights exp2(arg) and
+    //           their E4M3 packing;
+    //  block C: tile t's P.V and l MFMAs beside tile t+1's row max,
+    //           running-max decision and exp2 arguments (written over sb);
+    //  then the rare rescale branch.
+    // Scheduling fences fix the order: after every MFMA, one slice of the
+    // vector work.  The last tile of a wave still forms the scores of the
+    // stage after it (never used), so that a step is straight-line code.
+    constexpr int kSlotsA = 2 * G::kQSteps;  // MFMAs of block A
+    constexpr int kSlotsC = G::kOTiles + 1;  // MFMAs of block C
+    static_assert(kSlotsA == 4 && kSlotsC == 5, "the step's slices assume d = 128");
+    auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto step = [&](int t, int st_v, int st_k, f32x16 (&sa)[2], f32x16 (&sb)[2])
+                    __attribute__((always_inline)) {
+      const bool next = t + 1 < t_wave_end;
+      // V^T operands of tile t: read g (0..3) covers keys 32 (g/2) + 16 (g%2)
+      // + 8 hf + 0..7, the constant part of the address in the instruction.
+      const lds_char* Vst = lds + st_v * G::kStageBytes + G::kTileBytes;
+      u32x2 vr[4][G::kOTiles];
+      auto vread = [&](int g) __attribute__((always_inline)) {
+        const int off = (32 * (g >> 1) + 16 * (g & 1)) * D;
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2)
+          vr[g][t2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                                    (lds_i32x2*)(Vst + v_off[t2] + off)));
+      };
+      // K operands of tile t+1.
+      const lds_char* Kst = lds + st_k * G::kStageBytes;
+      u32x8 ka[G::kQSteps][2];
+      auto kread = [&](int ks) __attribute__((always_inline)) {
+        ka[ks][0] = cat(*(const lds_u32x4*)(Kst + k_off[ks][0]),
+                        *(const lds_u32x4*)(Kst + k_off[ks][1]));
+        ka[ks][1] = cat(*(const lds_u32x4*)(Kst + k_off[ks][0] + 32 * D),
+                        *(const lds_u32x4*)(Kst + k_off[ks][1] + 32 * D));
+      };
+
+      // ---------------- block A ----------------
+      // Word w of the E4M3 weights holds elements 4 (w % 4) .. +3 of score
+      // block w / 4 (the B-operand order, see the packing in finish()).
+      // Item c: the exponentials of word c (c < 8) and the packing of word
+      // c - 1 (c >= 1).
+      float pe[2][4];
+      u32x8 pb;
+      auto valu_a = [&](int cc) __attribute__((always_inline)) {
+        if (cc < 8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pe[cc & 1][e] = fast_exp2(sa[cc >> 2][4 * (cc & 3) + e]);
+        }
+        if (cc >= 1) {
+          const int wd = cc - 1, h2 = wd & 1;
+          // The first conversion keeps the upper half of its destination,
+          // which the second one overwrites: it may be any register, and
+          // pe[h2][0]'s, which dies here, saves clearing one.
+          const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(pe[h2][0], pe[h2][1],
+                                                              __float_as_uint(pe[h2][0]), false);
+          pb[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(pe[h2][2], pe[h2][3], lo, true);
+        }
+      };
+      // Item 0 before the first MFMA, while its K operands are read; then
+      // two items after each MFMA, the next k-step's K operands one step
+      // ahead, and the V^T reads once the first K operands are consumed.
+      kread(0);
+      valu_a(0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) asm volatile("" ::"v"(pe[0][e]));  // before the first MFMA
+      fence();
+#pragma unroll
+      for (int slot = 0; slot < kSlotsA; ++slot) {
+        const int ks = slot >> 1, hh = slot & 1;
+        sb[hh] = mfma_fp8(ka[ks][hh], qT[ks], ks == 0 ? f32x16{} : sb[hh]);
+        fence();
+        valu_a(2 * slot + 1);
+        valu_a(2 * slot + 2);
+        if (hh == 0 && ks + 1 < G::kQSteps) kread(ks + 1);
+        if (slot == 1) {
+          vread(0);
+          vread(1);
+        }
+        if (slot == 2) {
+          vread(2);
+          vread(3);
+        }
+        fence();
+      }
+      // The weights are formed here, beside the MFMAs: an empty use keeps
+      // the compiler from sinking them below the branch that follows.
+#pragma unroll
+      for (int wd = 0; wd < 8; ++wd) asm volatile("" ::"v"(pb[wd]));
+
+      if (__builtin_expect(next && needs_mask(t + 1), 0)) mask(t + 1, sb);
+
+      // ---------------- block C ----------------
+      // Items: the row max of each score block (0, 1), the running-max
+      // decision (2), the exp2 arguments in four parts (3-6).
+      float mh[2];
+      float m_new = m_run;
+      const float raise_above = next ? m_run + kSlack : __builtin_inff();
+      bool raise = false;
+      auto valu_c = [&](int cc) __attribute__((always_inline)) {
+        if (cc < 2) mh[cc] = max16(sb[cc]);
+        if (cc == 2) {
+          const float mxc = max_xor32(fmaxf(mh[0], mh[1])) * c_scale;
+          raise = mxc > raise_above;  // never for the surplus tile
+          m_new = raise ? mxc : m_run;
+        }
+        if (cc >= 3) {
+          const int i0 = 8 * (cc - 3);
+#pragma unroll
+          for (int i = i0; i < i0 + 8; ++i)
+            sb[i >> 4][i & 15] = fmaf(sb[i >> 4][i & 15], c_scale, -m_new);
+        }
+      };
+      // Items after MFMAs 0 .. 4: {0}, {1}, {2, 3}, {4}, {5, 6}.
+#pragma unroll
+      for (int slot = 0; slot < kSlotsC; ++slot) {
+        if (slot < G::kOTiles) {
+          const int t2 = slot;
+          const u32x8 va = {vr[0][t2][0], vr[0][t2][1], vr[1][t2][0], vr[1][t2][1],
+                            vr[2][t2][0], vr[2][t2][1], vr[3][t2][0], vr[3][t2][1]};
+          acc[t2] = mfma_fp8(va, pb, acc[t2]);
+        } else {
+          lacc = mfma_fp8(ones, pb, lacc);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 7; ++cc)
+          if (((cc + 1) * kSlotsC - 1) / 7 == slot) valu_c(cc);
+        fence();
+      }
+      // The arguments are formed here, beside the MFMAs (see above).
+#pragma unroll
+      for (int i = 0; i < 32; ++i) asm volatile("" ::"v"(sb[i >> 4][i & 15]));
+      if (__builtin_expect(__any(raise), 0)) {
+        asm volatile("" ::: "memory");  // a real branch, not a speculated rescale
+        const float alpha = fast_exp2(m_run - m_new);  // 1 for rows that kept m
+#pragma unroll
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2] *= alpha;
+        lacc *= alpha;
+      }
+      m_run = m_new;
+    };
+
+    f32x16 sa[2], sb[2];
+    // Prologue: tile t_begin's scores and arguments (acc and l are still
+    // zero: nothing to rescale).
+    if (t_begin < t_wave_end) {
+      scores(0, sa);
+      if (needs_mask(t_begin)) mask(t_begin, sa);
+      const float mxc = max_xor32(fmaxf(max16(sa[0]), max16(sa[1]))) * c_scale;
+      m_run = fmaxf(mxc, m_run);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) sa[i >> 4][i & 15] = fmaf(sa[i >> 4][i & 15], c_scale, -m_run);
+    }
+    int s0 = 0;  // ring stage of tile t
+    for (int t = t_begin; t < t_end; t += kGroup8) {
+#pragma unroll
+      for (int g = 1; g <= kGroup8; ++g)
+        if (t + kGroup8 + g < t_end) issue_tile(t + kGroup8 + g, ring(s0 + kGroup8 + g));
+#pragma unroll
+      for (int g = 0; g < kGroup8; ++g) {
+        if (t + g < t_wave_end) {
+          // The two score buffers swap roles from step to step.
+          if (g % 2 == 0) step(t + g, ring(s0 + g), ring(s0 + g + 1), sa, sb);
+          else step(t + g, ring(s0 + g), ring(s0 + g + 1), sb, sa);
+        }
+      }
+      static_assert(kGroup8 % 2 == 0, "the arguments are back in sa after a group");
+      // This wave's DMAs are done and its LDS reads finished: after the
+      // barrier tiles t+kGroup8 .. t+2 kGroup8 are readable and the stages
+      // of tiles t .. t+kGroup8-1 free.
+      wait_vm_lgkm0<0>();
+      bare_barrier();
+      s0 = ring(s0 + kGroup8);
+    }
   }
-#endif
 
   // -------- epilogue: O = acc * v_descale / l, zero for rows without keys --------
   if (qrow >= n) return;
