@@ -52,6 +52,11 @@ CASES = [
     ("d64_noncausal_f16", "f16", 1, 4, 4, 129, 129, 64, False, 1.0, None),
     ("single_row", "bf16", 1, 1, 1, 1, 1, 128, True, 1.0, None),
     ("single_key_d64", "bf16", 1, 2, 2, 70, 1, 64, False, 1.0, None),
+    # the pipelined key loop (d = 128): grouped heads with a causal tail, and
+    # fewer keys than queries with a partial last tile
+    ("gqa_d128_causal_tail", "bf16", 2, 8, 2, 190, 190, 128, True, 1.0, None),
+    ("m_lt_n_d128_f16", "f16", 1, 2, 2, 333, 70, 128, False, 1.0, None),
+    ("hot_leftpad_d128", "bf16", 3, 2, 2, 390, 390, 128, True, 10.0, [390, 200, 65]),
 ]
 
 
