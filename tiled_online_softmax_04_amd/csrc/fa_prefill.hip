@@ -90,6 +90,24 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// The b-th longest of a batch's B sequences (lengths clamped to [0, cap], ties
+// by index), for batches of up to 64: the workgroups of the longest
+// sequences are handed out first, so that the short ones fill the end of the
+// launch.  Larger batches keep their order.  Wave-uniform.
+__device__ __forceinline__ int kth_longest(int b, const int32_t* __restrict__ lens, int B,
+                                           int cap) {
+  if (B > 64) return b;
+  const int lane = threadIdx.x & 63;
+  const int mine = lane < B ? min(max(lens[lane], 0), cap) : -1;
+  int rank = 0;
+  for (int i = 0; i < B; ++i) {
+    const int li = __builtin_amdgcn_readlane(mine, i);
+    rank += (li > mine || (li == mine && i < lane)) ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(lane < B && rank == b);
+  return hit ? __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) : b;
+}
+
 // PARTIAL: attend only to keys in [key_begin, key_end) and write the result
 // normalised over that range as float32 (Of) together with the natural-log
 // softmax denominator of the range (Lse), instead of the final O.
@@ -128,7 +146,11 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   const int qt_ord = logical % q_tiles;
   // Causal tiles further down hold more keys: hand those out first.
   const int qt = CAUSAL ? q_tiles - 1 - qt_ord : qt_ord;
-  const int b = bh / Hq, h = bh % Hq;
+  const int h = bh % Hq;
+  // Sequences of different lengths: the longest first (see kth_longest).
+  const int b = (RAGGED || PAGED)
+                    ? kth_longest(bh / Hq, seq_lens, total / (Hq * q_tiles), RAGGED ? n : maxb * bs)
+                    : bh / Hq;
   const int hkv = h / group;
   const int Hkv = Hq / group;
 
