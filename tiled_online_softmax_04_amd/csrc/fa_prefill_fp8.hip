@@ -11,9 +11,9 @@
 // that write LDS directly, two tiles (or pipeline steps) per barrier.  At
 // d = 128 the key loop is a software pipeline, as in the 16-bit kernel: each
 // step issues the next tile's score MFMAs beside this tile's exponentials and
-// E4M3 packing, then this tile's P.V MFMAs beside the next tile's row max and
-// exp2 arguments (five stages: the tiles of both steps and the one whose
-// scores the second step forms, while the next two land).  At d = 64 a step
+// E4M3 packing, then this tile's P.V MFMAs beside the next tile's exp2
+// arguments (five stages: the tiles of both steps and the one whose scores
+// the second step forms, while the next two land).  At d = 64 a step
 // would hold half as many MFMAs for the same vector work, and whole tiles are
 // computed in turn from one half of a four-stage ring while the other lands.
 // Both products run on v_mfma_f32_32x32x64_f8f6f4 (64 fp8 products per lane
@@ -29,10 +29,14 @@
 //
 // Scales: the fp32 scores are exact sums of code products; c = scale *
 // q_descale * k_descale * log2(e) turns them into log2-domain scores, and the
-// epilogue multiplies by v_descale / l.  The running max is raised lazily
-// (slack 8, as in the 16-bit kernel), so weights stay at most 2^8 = 256: inside
-// the E4M3 range (finite up to 448; the conversion gives NaN only from 464
-// up) and, for the key at the row max, an exact power of two.
+// epilogue multiplies by v_descale / l.  The running max is raised lazily.
+// The d = 64 loop raises it when a tile's max beats it by more than 8 (as in
+// the 16-bit kernel), so weights stay at most 2^8 = 256.  The pipelined d = 128
+// loop forms no tile max at all: it exponentiates against the running max as
+// it stands and raises it only when a weight reached 464, the first value the
+// E4M3 conversion turns into NaN (the format has no infinity; finite values
+// end at 448), which the l product then carries.  Weights from 448 up to 464
+// round to 448, within the format's 2^-4 relative rounding.
 
 #include "fa_common.h"
 #include "fa_launch.h"
@@ -408,16 +412,16 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
     // One step of the pipeline.  On entry sa holds tile t's exp2 arguments
     // s * c - m (formed in the step before, or the prologue).
     //  block A: tile t+1's S^T MFMAs beside tile t's weights exp2(arg) and
-    //           their E4M3 packing;
-    //  block C: tile t's P.V and l MFMAs beside tile t+1's row max,
-    //           running-max decision and exp2 arguments (written over sb);
-    //  then the rare rescale branch.
+    //           their E4M3 packing, then tile t's l MFMA;
+    //  the rare branch that raises the running max (see the file header);
+    //  block C: tile t's P.V MFMAs beside tile t+1's exp2 arguments
+    //           (written over sb).
     // Scheduling fences fix the order: after every MFMA, one slice of the
     // vector work.  The last tile of a wave still forms the scores of the
     // stage after it (never used), so that a step is straight-line code.
     constexpr int kSlotsA = 2 * G::kQSteps;  // MFMAs of block A
-    constexpr int kSlotsC = G::kOTiles + 1;  // MFMAs of block C
-    static_assert(kSlotsA == 4 && kSlotsC == 5, "the step's slices assume d = 128");
+    constexpr int kSlotsC = G::kOTiles;      // MFMAs of block C
+    static_assert(kSlotsA == 4 && kSlotsC == 4, "the step's slices assume d = 128");
     auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
     auto step = [&](int t, int st_v, int st_k, f32x16 (&sa)[2], f32x16 (&sb)[2])
                     __attribute__((always_inline)) {
@@ -495,57 +499,52 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
       // the compiler from sinking them below the branch that follows.
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) asm volatile("" ::"v"(pb[wd]));
+      const float l_old = lacc[0];
+      lacc = mfma_fp8(ones, pb, lacc);
+      fence();
 
       if (__builtin_expect(next && needs_mask(t + 1), 0)) mask(t + 1, sb);
 
-      // ---------------- block C ----------------
-      // Items: the row max of each score block (0, 1), the running-max
-      // decision (2), the exp2 arguments in four parts (3-6).
-      float mh[2];
-      float m_new = m_run;
-      const float raise_above = next ? m_run + kSlack : __builtin_inff();
-      bool raise = false;
-      auto valu_c = [&](int cc) __attribute__((always_inline)) {
-        if (cc < 2) mh[cc] = max16(sb[cc]);
-        if (cc == 2) {
-          const float mxc = max_xor32(fmaxf(mh[0], mh[1])) * c_scale;
-          raise = mxc > raise_above;  // never for the surplus tile
-          m_new = raise ? mxc : m_run;
-        }
-        if (cc >= 3) {
-          const int i0 = 8 * (cc - 3);
+      // A weight that reached 464 converted to NaN (E4M3 has no infinity),
+      // and the l product carried it: the tile beat the running max by more
+      // than log2(464).  Rare: raise the max of the rows whose arguments pass
+      // kSlack to their tile max, rescale, and form the weights again.
+      const uint32_t lbits = __float_as_uint(lacc[0]) & 0x7fffffffu;
+      if (__builtin_expect(__any(lbits > 0x7f800000u), 0)) {
+        asm volatile("" ::: "memory");  // a real branch
+        const float a_max = max_xor32(fmaxf(max16(sa[0]), max16(sa[1])));
+        const float shift = a_max > kSlack ? a_max : 0.f;
+        const float alpha = fast_exp2(-shift);
 #pragma unroll
-          for (int i = i0; i < i0 + 8; ++i)
-            sb[i >> 4][i & 15] = fmaf(sb[i >> 4][i & 15], c_scale, -m_new);
-        }
-      };
-      // Items after MFMAs 0 .. 4: {0}, {1}, {2, 3}, {4}, {5, 6}.
+        for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sa[i >> 4][i & 15] -= shift;
+#pragma unroll
+        for (int cc = 0; cc < 9; ++cc) valu_a(cc);
+        const float l_new = l_old * alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lacc[i] = l_new;
+        lacc = mfma_fp8(ones, pb, lacc);
+        m_run += shift;
+      }
+
+      // ---------------- block C ----------------
+      // The exp2 arguments of tile t+1 against the running max, 8 after each
+      // P.V MFMA.
 #pragma unroll
       for (int slot = 0; slot < kSlotsC; ++slot) {
-        if (slot < G::kOTiles) {
-          const int t2 = slot;
-          const u32x8 va = {vr[0][t2][0], vr[0][t2][1], vr[1][t2][0], vr[1][t2][1],
-                            vr[2][t2][0], vr[2][t2][1], vr[3][t2][0], vr[3][t2][1]};
-          acc[t2] = mfma_fp8(va, pb, acc[t2]);
-        } else {
-          lacc = mfma_fp8(ones, pb, lacc);
-        }
+        const int t2 = slot;
+        const u32x8 va = {vr[0][t2][0], vr[0][t2][1], vr[1][t2][0], vr[1][t2][1],
+                          vr[2][t2][0], vr[2][t2][1], vr[3][t2][0], vr[3][t2][1]};
+        acc[t2] = mfma_fp8(va, pb, acc[t2]);
 #pragma unroll
-        for (int cc = 0; cc < 7; ++cc)
-          if (((cc + 1) * kSlotsC - 1) / 7 == slot) valu_c(cc);
+        for (int i = 8 * slot; i < 8 * slot + 8; ++i)
+          sb[i >> 4][i & 15] = fmaf(sb[i >> 4][i & 15], c_scale, -m_run);
         fence();
       }
       // The arguments are formed here, beside the MFMAs (see above).
 #pragma unroll
       for (int i = 0; i < 32; ++i) asm volatile("" ::"v"(sb[i >> 4][i & 15]));
-      if (__builtin_expect(__any(raise), 0)) {
-        asm volatile("" ::: "memory");  // a real branch, not a speculated rescale
-        const float alpha = fast_exp2(m_run - m_new);  // 1 for rows that kept m
-#pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) acc[t2] *= alpha;
-        lacc *= alpha;
-      }
-      m_run = m_new;
     };
 
     f32x16 sa[2], sb[2];
