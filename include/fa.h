@@ -229,9 +229,9 @@ size_t fa_paged_decode_workspace_size(int num_seqs, int heads_q, int heads_kv, i
  *
  * Query head h reads KV head h / (heads_q / heads_kv).
  * Limits of this build: dtype f16 or bf16 (f32 -> FA_ERR_UNSUPPORTED); d == dv,
- * d in {64, 128}; at most 65535 key splits per sequence (512 keys each, fewer
+ * d in {64, 128}; at most 65535 key splits per sequence (768 keys each, fewer
  * when the batch is small), i.e. max_blocks_per_seq * block_size up to about
- * 33.5 million keys (else FA_ERR_UNSUPPORTED).
+ * 50 million keys for a large batch (else FA_ERR_UNSUPPORTED).
  * FA_ERR_INVALID: null pointers for non-empty work, non-positive block_size,
  *   num_blocks or max_blocks_per_seq, negative sizes, heads_q % heads_kv != 0,
  *   non-finite or non-positive scale, misaligned pointers, a cache of 2^32 or

@@ -210,14 +210,14 @@ def test_noalloc_scratch_limit_matches_header():
 
 
 def test_decode_workspace_size(lib):
-    # 64 sequences x 32 query heads, up to 512 blocks of 16 keys: 512-key splits
-    # -> 16 splits, each holding m, l and o[128] in float32
-    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 16 * (8 + 512)
+    # 64 sequences x 32 query heads, up to 512 blocks of 16 keys: 768-key splits
+    # -> 11 splits, each holding m, l and o[128] in float32
+    assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 512, 16) == 64 * 32 * 11 * (8 + 512)
     assert lib.fa_paged_decode_workspace_size(64, 32, 8, 128, 0, 16) == 0
     assert lib.fa_paged_decode_workspace_size(64, 32, 0, 128, 512, 16) == 0
     # a lone sequence gets smaller splits so the GPU still fills
     one = lib.fa_paged_decode_workspace_size(1, 32, 8, 128, 512, 16)
-    assert one > 32 * 16 * (8 + 512)
+    assert one > 32 * 11 * (8 + 512)
 
 
 def test_binding_rejects_host_tensors():
