@@ -43,6 +43,11 @@ CASES = [
     ("bf16_bs32_noncausal", "bf16", 2, 8, 8, 64, 32, [257, 64], 16, 90, False),
     ("f16_d64_gqa_causal", "f16", 4, 16, 4, 64, 16, [1, 33, 129, 250], 20, 17, True),
     ("bf16_whole_sequence", "bf16", 2, 2, 2, 128, 16, [256, 256], 16, 256, True),
+    # block sizes around the 64-key tile: a block per tile, blocks wider than a
+    # tile, one key per block, and a ragged last tile in each
+    ("bf16_bs64_causal", "bf16", 2, 4, 2, 128, 64, [450, 130], 8, 200, True),
+    ("f16_bs128_noncausal", "f16", 2, 4, 4, 128, 128, [333, 129], 4, 70, False),
+    ("bf16_bs1_causal", "bf16", 2, 2, 1, 64, 1, [150, 70], 160, 40, True),
     # block tables of up to 8192 entries take the pipelined loop (the table fills the
     # LDS beside the four-stage ring at 8192); larger ones the one-tile-per-barrier loop
     ("bf16_table_8192", "bf16", 2, 4, 1, 128, 16, [500, 1200], 8192, 150, True),

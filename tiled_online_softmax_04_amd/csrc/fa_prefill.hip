@@ -232,9 +232,39 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
     __syncthreads();
   }
   const uint16_t* const cache_dma = dma_v ? V : K;
+  // Paged, block size a power of two that divides the 64-key tile: a lane's
+  // row keeps its offset inside its block from tile to tile, and its block is
+  // table entry t * (64 / bs) + (key >> log2 bs).  The byte offset of the row
+  // inside the block (head and columns included) is fixed per lane.
+  const bool pg_fast = PAGED && bs_shift >= 0 && bs <= kBc;
+  uint32_t pg_off[G::kDmaPerWave];
+  const uint64_t pg_blk_bytes = (uint64_t)bs * (uint64_t)Hkv * D * 2;
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i)
+      pg_off[i] = pg_fast ? (uint32_t)((((uint32_t)(dma_key[i] & (bs - 1)) * (uint32_t)Hkv +
+                                         (uint32_t)hkv) * D + (uint32_t)dma_col[i]) * 2u)
+                          : 0u;
+  }
   auto issue_tile = [&](int t, int st) {
     lds_char* dst = lds + st * G::kStageElems * 2 + dma_lds0;
     if constexpr (PAGED) {
+      if (pg_fast && (t + 1) * kBc <= kv_end) {
+        // Every row of the tile is a key this workgroup needs: the table
+        // entries first, one wait, then the copies.
+        const int e0 = t << (6 - bs_shift);
+        uint32_t ent[G::kDmaPerWave];
+#pragma unroll
+        for (int i = 0; i < G::kDmaPerWave; ++i) ent[i] = (uint32_t)bt_s[e0 + (dma_key[i] >> bs_shift)];
+#pragma unroll
+        for (int i = 0; i < G::kDmaPerWave; ++i) {
+          const uint64_t a = (uint64_t)(uintptr_t)cache_dma + (uint64_t)ent[i] * pg_blk_bytes + pg_off[i];
+          gdma16_untracked((const void*)(uintptr_t)a,
+                           (uint32_t)__builtin_amdgcn_readfirstlane(
+                               (uint32_t)(uintptr_t)(dst + i * G::kRowsPerDma * D * 2)));
+        }
+        return;
+      }
       // Each row through the table; rows past the keys this workgroup needs
       // repeat its last key (masked later) so no address leaves the cache.
 #pragma unroll
