@@ -110,6 +110,51 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
 
+// A wave's 32 rows of output leave through LDS, so that every store
+// instruction writes whole rows.  In the 32x32 accumulator layout lane l holds
+// pieces of row l & 31, so one store straight from the accumulators would put
+// 8 or 16 bytes into each of 32 rows.  Instead the wave writes its rows into
+// kBytes of LDS of its own (16-byte chunks XOR-swizzled by row, so that
+// neither these writes nor the row-wise reads meet bank conflicts), then
+// reads them back kChunks lanes per row and stores kRowsPerRead whole rows per
+// instruction.
+template <int kRowBytes>
+struct RowStage {
+  static_assert(kRowBytes == 128 || kRowBytes == 256 || kRowBytes == 512, "row size");
+  static constexpr int kChunks = kRowBytes / 16;
+  static constexpr int kRowsPerRead = 64 / kChunks;
+  static constexpr int kReads = 32 / kRowsPerRead;
+  static constexpr int kBytes = 32 * kRowBytes;
+  // LDS byte offset of byte `col` (a multiple of 8) of row r.
+  __device__ static __forceinline__ uint32_t at(int r, int col) {
+    const int sw = kRowBytes == 128 ? (r >> 1) & 7 : r & 15;
+    return (uint32_t)(r * kRowBytes + (((col >> 4) ^ sw) << 4) + (col & 15));
+  }
+  template <class V>
+  __device__ static __forceinline__ void put(lds_char* ob, int r, int col, V v) {
+    typedef __attribute__((address_space(3))) V lds_v;
+    *(lds_v*)(ob + at(r, col)) = v;
+  }
+  // Rows r < rows go to dst + r * stride (bytes).  Only this wave uses ob, so
+  // waiting for its own LDS writes is enough; the clobber keeps the compiler
+  // from moving the reads above them.
+  __device__ static __forceinline__ void store(const lds_char* ob, int lane, char* dst,
+                                               size_t stride, int rows) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int rr = lane / kChunks, cc = lane % kChunks;
+    u32x4 x[kReads];
+#pragma unroll
+    for (int i = 0; i < kReads; ++i)
+      x[i] = *(const lds_u32x4*)(ob + at(i * kRowsPerRead + rr, cc * 16));
+    char* const d0 = dst + cc * 16;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i) {
+      const int r = i * kRowsPerRead + rr;
+      if (r < rows) *reinterpret_cast<u32x4*>(d0 + (size_t)r * stride) = x[i];
+    }
+  }
+};
+
 // Workgroup barrier without a memory fence: the caller has already waited for
 // its own LDS traffic; the empty asm statements keep the compiler from moving
 // memory accesses across it.

@@ -806,51 +806,63 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 
   // -------- epilogue: O = acc / l, zero for rows without keys --------
   if constexpr (PARTIAL) {
-    // float32 O of the range and lse = ln(2^m * l) (m is in log2 units).
+    // float32 O of the range and lse = ln(2^m * l) (m is in log2 units); O
+    // leaves through the idle ring, whole rows per store (RowStage).
+    using RS = RowStage<D * 4>;
+    static_assert(kWaves * kNT * RS::kBytes <= kRing * G::kStageElems * 2, "staged O fits the ring");
+    wait_vm_lgkm0<0>();
+    bare_barrier();  // every wave is done with the ring
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const float l_tot = sum_xor32(l_run[nt]);
       const bool has = l_tot > 0.f && q_ok[nt];
       const float inv = has ? 1.f / l_tot : 0.f;
-      if (qrow[nt] < n) {
-        float* orow = Of + q_base + (size_t)qrow[nt] * D;
-#pragma unroll
-        for (int t2 = 0; t2 < G::kOTiles; ++t2) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int dv0 = 32 * t2 + 8 * g + 4 * hf;
-            float4 x;
-            x.x = acc[t2][nt][4 * g] * inv;
-            x.y = acc[t2][nt][4 * g + 1] * inv;
-            x.z = acc[t2][nt][4 * g + 2] * inv;
-            x.w = acc[t2][nt][4 * g + 3] * inv;
-            *reinterpret_cast<float4*>(orow + dv0) = x;
-          }
-        }
-        if (hf == 0)
-          Lse[q_base / D + qrow[nt]] =
-              has ? (m_run[nt] + log2f(l_tot)) * kLn2 : -__builtin_inff();
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const float l_tot = sum_xor32(l_run[nt]);
-    const float inv = (l_tot > 0.f && q_ok[nt]) ? 1.f / l_tot : 0.f;
-    if (qrow[nt] < n) {
-      uint16_t* orow = O + q_base + (size_t)qrow[nt] * D;
+      lds_char* const ob = lds + (w * kNT + nt) * RS::kBytes;
 #pragma unroll
       for (int t2 = 0; t2 < G::kOTiles; ++t2) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int dv0 = 32 * t2 + 8 * g + 4 * hf;
-          const uint32_t lo = T::pack(acc[t2][nt][4 * g] * inv, acc[t2][nt][4 * g + 1] * inv);
-          const uint32_t hi = T::pack(acc[t2][nt][4 * g + 2] * inv, acc[t2][nt][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + dv0) = u32x2{lo, hi};
+          // columns 32 t2 + 8 g + 4 hf .. +3 of row ql
+          const u32x4 x = {__float_as_uint(acc[t2][nt][4 * g] * inv),
+                           __float_as_uint(acc[t2][nt][4 * g + 1] * inv),
+                           __float_as_uint(acc[t2][nt][4 * g + 2] * inv),
+                           __float_as_uint(acc[t2][nt][4 * g + 3] * inv)};
+          RS::put(ob, ql, (32 * t2 + 8 * g + 4 * hf) * 4, x);
         }
       }
+      const int r0 = wq0 + 32 * nt;
+      RS::store(ob, lane, reinterpret_cast<char*>(Of + q_base + (size_t)r0 * D), (size_t)D * 4,
+                n - r0);
+      if (hf == 0 && qrow[nt] < n)
+        Lse[q_base / D + qrow[nt]] =
+            has ? (m_run[nt] + log2f(l_tot)) * kLn2 : -__builtin_inff();
     }
+    return;
+  }
+  // Through the (now idle) K/V ring, whole rows per store (RowStage):
+  // measured 3.7% faster at 2048 keys than storing from the accumulators.
+  using RS = RowStage<D * 2>;
+  static_assert(kWaves * kNT * RS::kBytes <= kRing * G::kStageElems * 2, "staged O fits the ring");
+  wait_vm_lgkm0<0>();
+  bare_barrier();  // every wave is done with the ring
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const float l_tot = sum_xor32(l_run[nt]);
+    const float inv = (l_tot > 0.f && q_ok[nt]) ? 1.f / l_tot : 0.f;
+    lds_char* const ob = lds + (w * kNT + nt) * RS::kBytes;
+#pragma unroll
+    for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // columns 32 t2 + 8 g + 4 hf .. +3 of row ql
+        const uint32_t lo = T::pack(acc[t2][nt][4 * g] * inv, acc[t2][nt][4 * g + 1] * inv);
+        const uint32_t hi = T::pack(acc[t2][nt][4 * g + 2] * inv, acc[t2][nt][4 * g + 3] * inv);
+        RS::put(ob, ql, (32 * t2 + 8 * g + 4 * hf) * 2, u32x2{lo, hi});
+      }
+    }
+    const int r0 = wq0 + 32 * nt;
+    RS::store(ob, lane, reinterpret_cast<char*>(O + q_base + (size_t)r0 * D), (size_t)D * 2,
+              n - r0);
   }
 }
 

@@ -582,27 +582,42 @@ __global__ __launch_bounds__(kT8, 2) void fa_fwd_fp8(
   }
 
   // -------- epilogue: O = acc * v_descale / l, zero for rows without keys --------
-  if (qrow >= n) return;
   const float l = lacc[0];
   const float f = (l > 0.f && q_ok) ? v_descale / l : 0.f;
+  if constexpr (OUT == 0) {
+    // float32 rows: twice the ring's room, so straight from the accumulators
+    if (qrow >= n) return;
 #pragma unroll
-  for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+    for (int t2 = 0; t2 < G::kOTiles; ++t2) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dv0 = 32 * t2 + 8 * g + 4 * hf;
-      const size_t off = q_base + (size_t)qrow * D + dv0;
-      const float x0 = acc[t2][4 * g] * f, x1 = acc[t2][4 * g + 1] * f;
-      const float x2 = acc[t2][4 * g + 2] * f, x3 = acc[t2][4 * g + 3] * f;
-      if constexpr (OUT == 0) {
-        *reinterpret_cast<float4*>(static_cast<float*>(O) + off) = float4{x0, x1, x2, x3};
-      } else if constexpr (OUT == 1) {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(O) + off) =
-            u32x2{F16::pack(x0, x1), F16::pack(x2, x3)};
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(O) + off) =
-            u32x2{BF16::pack(x0, x1), BF16::pack(x2, x3)};
+      for (int g = 0; g < 4; ++g) {
+        const size_t off = q_base + (size_t)qrow * D + 32 * t2 + 8 * g + 4 * hf;
+        *reinterpret_cast<float4*>(static_cast<float*>(O) + off) =
+            float4{acc[t2][4 * g] * f, acc[t2][4 * g + 1] * f, acc[t2][4 * g + 2] * f,
+                   acc[t2][4 * g + 3] * f};
       }
     }
+  } else {
+    // 16-bit rows leave through the idle ring, whole rows per store (RowStage).
+    using RS = RowStage<D * 2>;
+    static_assert(kW8 * RS::kBytes <= kRing8 * G::kStageBytes, "staged O fits the ring");
+    using T = typename std::conditional<OUT == 1, F16, BF16>::type;
+    wait_vm_lgkm0<0>();
+    bare_barrier();  // every wave is done with the ring
+    lds_char* const ob = lds + w * RS::kBytes;
+#pragma unroll
+    for (int t2 = 0; t2 < G::kOTiles; ++t2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // columns 32 t2 + 8 g + 4 hf .. +3 of row ql
+        const uint32_t lo = T::pack(acc[t2][4 * g] * f, acc[t2][4 * g + 1] * f);
+        const uint32_t hi = T::pack(acc[t2][4 * g + 2] * f, acc[t2][4 * g + 3] * f);
+        RS::put(ob, ql, (32 * t2 + 8 * g + 4 * hf) * 2, u32x2{lo, hi});
+      }
+    }
+    RS::store(ob, lane,
+              reinterpret_cast<char*>(static_cast<uint16_t*>(O) + q_base + (size_t)wq0 * D),
+              (size_t)D * 2, n - wq0);
   }
 }
 
