@@ -294,14 +294,18 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       if (t_begin + i < t_end) issue_tile(t_begin + i, i);
   }
 
-  // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive d.
+  // Queries as B operands of S^T = K Q^T: lane holds column ql, 8 consecutive
+  // d.  The pipelined loop brings them in through LDS (below); the other loop
+  // loads them straight into registers.
   u32x4 qT[kNT][G::kQSteps];
+  if constexpr (PG == 2) {
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-    for (int ks = 0; ks < G::kQSteps; ++ks)
-      qT[nt][ks] = q_ok[nt] ? load16(Qh + (size_t)qrow[nt] * D + ks * 16 + hf * 8)
-                            : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < G::kQSteps; ++ks)
+        qT[nt][ks] = q_ok[nt] ? load16(Qh + (size_t)qrow[nt] * D + ks * 16 + hf * 8)
+                              : u32x4{0, 0, 0, 0};
+  }
 
   f32x16 acc[G::kOTiles][kNT];
   float m_run[kNT], l_run[kNT];
@@ -524,20 +528,50 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       if (wq0 + qoff + kQPerWave - 1 < 0) t_wave_end = t_begin;
     t_wave_end = __builtin_amdgcn_readfirstlane(max(t_wave_end, t_begin));
 
-    // The query loads above go out before the first tiles.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (t_begin + i < t_end) issue_tile(t_begin + i, i);
-    // Loads complete in issue order: at most the DMAs of the tiles after
-    // t_begin may stay in flight.
+    // The wave's 32 query rows come in whole rows per DMA (a load straight
+    // into the B-operand layout would touch 32 rows per instruction) into its
+    // own part of ring stages 2 and 3, chunks swizzled as in a K tile, and
+    // are read back with the K-operand offsets.  Rows before the first real
+    // query (left pad, or before a paged sequence's first token) and rows
+    // from n on lie outside the buffer and read as zeros.
     {
-      const int after = min(2, t_end - t_begin - 1);
-      if (after >= 2) wait_vm_lgkm0<2 * G::kDmaPerWave>();
-      else if (after == 1) wait_vm_lgkm0<G::kDmaPerWave>();
-      else wait_vm_lgkm0<0>();
+      static_assert(kWaves * 32 * D * 2 <= 2 * G::kStageElems * 2, "queries fit stages 2 and 3");
+      constexpr int kQDma = 32 * D * 2 / 1024;
+      const int qpad = RAGGED ? pad : PAGED ? min(max(-qoff, 0), n) : 0;
+      const u32x4 rsrc_q =
+          make_rsrc_words(Qh + (size_t)qpad * D, (uint32_t)(n - qpad) * (uint32_t)(D * 2));
+      const uint32_t qs_addr = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds + 2 * G::kStageElems * 2 + w * (32 * D * 2)));
+#pragma unroll
+      for (int i = 0; i < kQDma; ++i) {
+        const int p = i * G::kRowsPerDma + lane / G::kChunks;
+        const int chunk = (lane % G::kChunks) ^ k_swz<D>(p);
+        // rows before qpad give a negative offset, which wraps out of range
+        dma16_untracked(rsrc_q, (uint32_t)(((wq0 - qpad + p) * D + chunk * 8) * 2),
+                        qs_addr + (uint32_t)(i * 1024));
+      }
     }
+    // Tiles t_begin and t_begin+1 follow; t_begin+2 goes to stage 2 once
+    // every wave has read its queries (after the barrier below).
+    const int pre = min(2, t_end - t_begin);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+    // Loads complete in issue order: the queries first.
+    if (pre == 2) wait_vm_lgkm0<2 * G::kDmaPerWave>();
+    else if (pre == 1) wait_vm_lgkm0<G::kDmaPerWave>();
+    else wait_vm_lgkm0<0>();
+    asm volatile("" ::: "memory");
+    {
+      const lds_char* const qs = lds + 2 * G::kStageElems * 2 + w * (32 * D * 2);
+#pragma unroll
+      for (int ks = 0; ks < G::kQSteps; ++ks) qT[0][ks] = *(const lds_u32x4*)(qs + k_off[ks]);
+    }
+    // Then tile t_begin; tile t_begin+1 may stay in flight.
+    if (pre == 2) wait_vm_lgkm0<G::kDmaPerWave>();
+    else wait_vm_lgkm0<0>();
     bare_barrier();
+    if (t_begin + 2 < t_end) issue_tile(t_begin + 2, 2);
 
     // LDS byte offsets of the MFMA operands from one register each.  The K
     // chunk of lane ql at k-step ks is (2 ks + hf) XOR the row's swizzle, so
