@@ -81,7 +81,8 @@ typedef enum {
  * FA_ERR_INVALID: a null tensor pointer (when the tensor is non-empty), negative
  *   sizes, heads_kv == 0 or heads_q % heads_kv != 0, causal or seq_lens with
  *   n != m, a non-finite or non-positive scale, misaligned pointers, an unknown
- *   dtype, or sizes beyond 2^31 elements per head dimension product.
+ *   dtype, or one head of q, k or v (n * d or m * d elements) spanning 2^31
+ *   bytes or more.
  * Empty work (batch, heads_q or n zero) returns FA_OK without launching.
  */
 fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void* o,
@@ -130,7 +131,8 @@ fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* 
  * the matrix cores; the softmax weights enter the P.V product rounded to E4M3
  * (about 2^-4 relative each), the one deliberate loss of this path.
  * FA_ERR_INVALID additionally for descales that are not finite and > 0, or
- * whose product with scale underflows float32.  Limits: d == dv in {64, 128}
+ * whose product with scale underflows float32 (the head-size limit of fa_fwd
+ * counts one byte per element here).  Limits: d == dv in {64, 128}
  * (else FA_ERR_UNSUPPORTED).
  */
 fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, fa_dtype out_dtype,
@@ -187,7 +189,8 @@ fa_status fa_merge(fa_dtype out_dtype, const float* o_parts, const float* lse_pa
  * the decode of fa_paged_decode.
  * Limits of this build: f16 or bf16 (f32 -> FA_ERR_UNSUPPORTED), d == dv in
  * {64, 128}, max_blocks_per_seq <= 16384 (else FA_ERR_UNSUPPORTED).
- * FA_ERR_INVALID: as fa_paged_decode, plus a negative n.  No workspace.
+ * FA_ERR_INVALID: as fa_paged_decode, plus a negative n or a chunk of one head
+ * (n * d 16-bit values) spanning 2^31 bytes or more.  No workspace.
  */
 fa_status fa_paged_prefill(fa_dtype dt, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* seq_lens, int block_size,

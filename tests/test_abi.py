@@ -87,6 +87,10 @@ def fwd(lib, dt=2, q=P, k=P, v=P, o=P, B=1, Hq=2, Hkv=2, n=128, m=128, d=128, dv
     (dict(scale=float("inf")), fa.FA_ERR_INVALID),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID),
     (dict(n=1 << 24, m=1 << 24), fa.FA_ERR_INVALID),
+    # one 16-bit head of 2^30 elements spans 2^31 bytes: past the 32-bit offsets
+    (dict(n=1 << 23, m=1 << 23), fa.FA_ERR_INVALID),
+    (dict(n=64, m=1 << 23), fa.FA_ERR_INVALID),
+    (dict(dt=0, n=1 << 22, m=1 << 22), fa.FA_ERR_INVALID),
     (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=128, dv=64), fa.FA_ERR_UNSUPPORTED),
     (dict(d=256, dv=256), fa.FA_ERR_UNSUPPORTED),
@@ -305,6 +309,7 @@ def pprefill(lib, dt=2, q=P, kc=P, vc=P, bt=P, sl=P, bs=16, S=4, Hq=8, Hkv=2, n=
     (dict(dt=0), fa.FA_ERR_UNSUPPORTED),
     (dict(d=96, dv=96), fa.FA_ERR_UNSUPPORTED),
     (dict(maxb=16385), fa.FA_ERR_UNSUPPORTED),
+    (dict(n=1 << 23), fa.FA_ERR_INVALID),   # one head's chunk spans 2^31 bytes
 ])
 def test_paged_prefill_rejects_before_launch(lib, kw, code):
     assert pprefill(lib, **kw) == code

@@ -27,7 +27,11 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
-constexpr long long kMaxElems = 1LL << 31;
+// One head's Q, K or V spans fewer than 2^31 bytes: the kernels address a head
+// through a buffer descriptor with 32-bit byte offsets, and the few rows they
+// read before a head's first valid row give negative offsets that must wrap
+// past 2^31 and so fall outside the buffer (reading zeros).
+constexpr long long kMaxHeadBytes = 1LL << 31;
 
 }  // namespace
 
@@ -52,7 +56,7 @@ const char* fa_last_error(void) { return g_last_error; }
 static fa_status check_fwd(fa_dtype dt, const void* q, const void* k, const void* v,
                            const void* o, int batch, int heads_q, int heads_kv, int n, int m,
                            int d, int dv, float scale, int causal, const int32_t* seq_lens,
-                           bool* empty) {
+                           bool* empty, long long in_bytes) {
   *empty = false;
   if (dt != FA_DTYPE_F32 && dt != FA_DTYPE_F16 && dt != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID, "unknown dtype %d", (int)dt);
@@ -68,9 +72,9 @@ static fa_status check_fwd(fa_dtype dt, const void* q, const void* k, const void
     return fail(FA_ERR_INVALID, "seq_lens (left padding) needs n == m (n=%d m=%d)", n, m);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
-  if ((long long)n * d >= kMaxElems || (long long)m * d >= kMaxElems ||
-      (long long)n * dv >= kMaxElems || (long long)m * dv >= kMaxElems)
-    return fail(FA_ERR_INVALID, "one head holds 2^31 elements or more");
+  if ((long long)n * d * in_bytes >= kMaxHeadBytes || (long long)m * d * in_bytes >= kMaxHeadBytes ||
+      (long long)m * dv * in_bytes >= kMaxHeadBytes)
+    return fail(FA_ERR_INVALID, "one head of q, k or v spans 2^31 bytes or more");
   if (!supported_head_dim(d) || dv != d)
     return fail(FA_ERR_UNSUPPORTED, "head dims d=%d dv=%d (need d == dv in {64, 128})", d, dv);
   if (batch == 0 || heads_q == 0 || n == 0) {
@@ -92,7 +96,7 @@ fa_status fa_fwd(fa_dtype dt, const void* q, const void* k, const void* v, void*
   g_last_error[0] = '\0';
   bool empty;
   const fa_status s = check_fwd(dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
-                                causal, seq_lens, &empty);
+                                causal, seq_lens, &empty, dt == FA_DTYPE_F32 ? 4 : 2);
   if (s != FA_OK || empty) return s;
   fa::FwdArgs a{(int)dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, scale, causal ? 1 : 0,
                 seq_lens, stream, 0, m, 0, nullptr, nullptr, 0, nullptr, 0, 0, 0};
@@ -110,7 +114,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, fa_dt
   // stand in for the element size, which the checks do not use).
   bool empty;
   fa_status s = check_fwd(out_dtype, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
-                          causal, seq_lens, &empty);
+                          causal, seq_lens, &empty, 1);
   if (s != FA_OK) return s;
   const float ds[3] = {q_descale, k_descale, v_descale};
   for (float x : ds)
@@ -137,7 +141,7 @@ fa_status fa_fwd_partial(fa_dtype dt, const void* q, const void* k, const void* 
   g_last_error[0] = '\0';
   bool empty;
   const fa_status s = check_fwd(dt, q, k, v, o, batch, heads_q, heads_kv, n, m, d, dv, scale,
-                                causal, seq_lens, &empty);
+                                causal, seq_lens, &empty, dt == FA_DTYPE_F32 ? 4 : 2);
   if (s != FA_OK) return s;
   if (key_begin < 0 || key_end < key_begin || key_end > m)
     return fail(FA_ERR_INVALID, "key range [%d, %d) outside [0, m = %d]", key_begin, key_end, m);
@@ -170,7 +174,7 @@ fa_status fa_paged_prefill(fa_dtype dt, const void* q, const void* k_cache, cons
   if (num_blocks <= 0) return fail(FA_ERR_INVALID, "num_blocks must be > 0");
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(FA_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
-  if ((long long)n * d >= kMaxElems) return fail(FA_ERR_INVALID, "chunk too long");
+  if ((long long)n * d * 2 >= kMaxHeadBytes) return fail(FA_ERR_INVALID, "chunk too long");
   if (dt == FA_DTYPE_F32) return fail(FA_ERR_UNSUPPORTED, "paged prefill supports f16 and bf16");
   if (max_blocks_per_seq > fa::max_paged_blocks())
     return fail(FA_ERR_UNSUPPORTED, "max_blocks_per_seq above %d", fa::max_paged_blocks());
