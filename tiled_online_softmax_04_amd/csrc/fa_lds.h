@@ -109,6 +109,28 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
+// The same for a wave-uniform count known only at run time (0..16).
+__device__ __forceinline__ void wait_vm_lgkm0_rt(int vm) {
+  switch (vm) {
+    case 1: wait_vm_lgkm0<1>(); break;
+    case 2: wait_vm_lgkm0<2>(); break;
+    case 3: wait_vm_lgkm0<3>(); break;
+    case 4: wait_vm_lgkm0<4>(); break;
+    case 5: wait_vm_lgkm0<5>(); break;
+    case 6: wait_vm_lgkm0<6>(); break;
+    case 7: wait_vm_lgkm0<7>(); break;
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 9: wait_vm_lgkm0<9>(); break;
+    case 10: wait_vm_lgkm0<10>(); break;
+    case 11: wait_vm_lgkm0<11>(); break;
+    case 12: wait_vm_lgkm0<12>(); break;
+    case 13: wait_vm_lgkm0<13>(); break;
+    case 14: wait_vm_lgkm0<14>(); break;
+    case 15: wait_vm_lgkm0<15>(); break;
+    case 16: wait_vm_lgkm0<16>(); break;
+    default: wait_vm_lgkm0<0>(); break;
+  }
+}
 
 // A wave's 32 rows of output leave through LDS, so that every store
 // instruction writes whole rows.  In the 32x32 accumulator layout lane l holds
@@ -135,17 +157,32 @@ struct RowStage {
     typedef __attribute__((address_space(3))) V lds_v;
     *(lds_v*)(ob + at(r, col)) = v;
   }
-  // Rows r < rows go to dst + r * stride (bytes).  Only this wave uses ob, so
-  // waiting for its own LDS writes is enough; the clobber keeps the compiler
-  // from moving the reads above them.
-  __device__ static __forceinline__ void store(const lds_char* ob, int lane, char* dst,
-                                               size_t stride, int rows) {
+  // The wave's rows back from ob, this lane's share in x.  Only this wave
+  // uses ob, so waiting for its own LDS writes is enough; the clobber keeps
+  // the compiler from moving the reads above them.
+  __device__ static __forceinline__ void read(const lds_char* ob, int lane, u32x4 (&x)[kReads]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int rr = lane / kChunks, cc = lane % kChunks;
-    u32x4 x[kReads];
 #pragma unroll
     for (int i = 0; i < kReads; ++i)
       x[i] = *(const lds_u32x4*)(ob + at(i * kRowsPerRead + rr, cc * 16));
+  }
+  // x (from read) as rows of a buffer whose range ends at the last row to
+  // write: exactly kReads store instructions, rows past the range dropped.
+  __device__ static __forceinline__ void store_buf(const u32x4 (&x)[kReads], int lane,
+                                                   __amdgpu_buffer_rsrc_t rsrc) {
+    const int rr = lane / kChunks, cc = lane % kChunks;
+#pragma unroll
+    for (int i = 0; i < kReads; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(x[i], rsrc, (i * kRowsPerRead + rr) * kRowBytes + cc * 16,
+                                             0, 0);
+  }
+  // Rows r < rows go to dst + r * stride (bytes).
+  __device__ static __forceinline__ void store(const lds_char* ob, int lane, char* dst,
+                                               size_t stride, int rows) {
+    u32x4 x[kReads];
+    read(ob, lane, x);
+    const int rr = lane / kChunks, cc = lane % kChunks;
     char* const d0 = dst + cc * 16;
 #pragma unroll
     for (int i = 0; i < kReads; ++i) {

@@ -29,6 +29,8 @@
 // "hot" data (scores of several hundred).  Scores, the running max and the
 // shifted exponent are float64; so are the weights and the accumulator.
 
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -133,15 +135,30 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   constexpr int kRing = ring_stages(PG == 2);
   extern __shared__ __align__(16) uint16_t smem[];
 
-  const int tid = threadIdx.x;
+  // Persistent form (dense, non-causal, full output): a launch of fewer
+  // workgroups than units, each taking units blockIdx.x, + gridDim.x, ...  A
+  // unit's output rows wait in registers and are stored after the next unit's
+  // query and first tile copies have gone out, so the stores overlap its start.
+  constexpr bool kPersist = !CAUSAL && !RAGGED && !PARTIAL && PG == 0;
+  using RS16 = RowStage<D * 2>;
+  u32x4 o_pend[RS16::kReads];
+  __amdgpu_buffer_rsrc_t o_pend_rsrc;
+  bool have_pend = false;
+
+  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+  int tid_ = threadIdx.x;
+  // Per unit, so that nothing lane-derived is kept live across units (which
+  // made the compiler spill).
+  if constexpr (kPersist) asm volatile("" : "+v"(tid_));
+  const int tid = tid_;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int ql = lane & 31, hf = lane >> 5;
 
   // Work units are (batch, query head, Q tile), Q tiles fastest; the units of
   // one KV group (batch, KV head) are consecutive.
-  const int logical = CAUSAL ? xcd_heavy_first(blockIdx.x, total, group * q_tiles, q_tiles)
-                             : xcd_by_group(blockIdx.x, total, group * q_tiles);
+  const int logical = CAUSAL ? xcd_heavy_first(unit, total, group * q_tiles, q_tiles)
+                             : xcd_by_group(unit, total, group * q_tiles);
   const int bh = logical / q_tiles;
   const int qt_ord = logical % q_tiles;
   // Causal tiles further down hold more keys: hand those out first.
@@ -557,19 +574,26 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       if (t_begin + i < t_end) issue_tile(t_begin + i, i);
+    // The previous unit's output rows (persistent form) go out behind them:
+    // always RS16::kReads store instructions, so the counts below are exact.
+    int stores = 0;
+    if constexpr (kPersist) {
+      if (have_pend) {
+        RS16::store_buf(o_pend, lane, o_pend_rsrc);
+        stores = RS16::kReads;
+        have_pend = false;
+      }
+    }
     // Loads complete in issue order: the queries first.
-    if (pre == 2) wait_vm_lgkm0<2 * G::kDmaPerWave>();
-    else if (pre == 1) wait_vm_lgkm0<G::kDmaPerWave>();
-    else wait_vm_lgkm0<0>();
+    wait_vm_lgkm0_rt(pre * G::kDmaPerWave + stores);
     asm volatile("" ::: "memory");
     {
       const lds_char* const qs = lds + 2 * G::kStageElems * 2 + w * (32 * D * 2);
 #pragma unroll
       for (int ks = 0; ks < G::kQSteps; ++ks) qT[0][ks] = *(const lds_u32x4*)(qs + k_off[ks]);
     }
-    // Then tile t_begin; tile t_begin+1 may stay in flight.
-    if (pre == 2) wait_vm_lgkm0<G::kDmaPerWave>();
-    else wait_vm_lgkm0<0>();
+    // Then tile t_begin; tile t_begin+1 and the stores may stay in flight.
+    wait_vm_lgkm0_rt((pre == 2 ? G::kDmaPerWave : 0) + stores);
     bare_barrier();
     if (t_begin + 2 < t_end) issue_tile(t_begin + 2, 2);
 
@@ -875,7 +899,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
   }
   // Through the (now idle) K/V ring, whole rows per store (RowStage):
   // measured 3.7% faster at 2048 keys than storing from the accumulators.
-  using RS = RowStage<D * 2>;
+  using RS = RS16;
   static_assert(kWaves * kNT * RS::kBytes <= kRing * G::kStageElems * 2, "staged O fits the ring");
   wait_vm_lgkm0<0>();
   bare_barrier();  // every wave is done with the ring
@@ -895,9 +919,24 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       }
     }
     const int r0 = wq0 + 32 * nt;
-    RS::store(ob, lane, reinterpret_cast<char*>(O + q_base + (size_t)r0 * D), (size_t)D * 2,
-              n - r0);
+    if constexpr (kPersist) {
+      static_assert(!kPersist || kNT == 1, "one pending row block per wave");
+      // Held until the next unit's copies are out (or the end of the launch).
+      RS::read(ob, lane, o_pend);
+      o_pend_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          O + q_base + (size_t)r0 * D, 0, max(n - r0, 0) * (D * 2), 0x00020000);
+      have_pend = true;
+    } else {
+      RS::store(ob, lane, reinterpret_cast<char*>(O + q_base + (size_t)r0 * D), (size_t)D * 2,
+                n - r0);
+    }
   }
+  if constexpr (!kPersist) break;  // one unit per workgroup: no loop at all
+  wait_lgkm0();
+  bare_barrier();  // every wave has its rows back: the next unit may refill the ring
+  }  // units
+  if constexpr (kPersist)
+    if (have_pend) RS16::store_buf(o_pend, threadIdx.x & 63, o_pend_rsrc);
 }
 
 // ---------------------------------------------------------------------------
@@ -1016,6 +1055,23 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
 constexpr int kMaxPagedBlocks = 16384;
 constexpr int kMaxPipelinedPagedBlocks = 8192;
 
+// Compute units of the current device, rounded down to a multiple of the 8
+// XCDs (so that workgroup i and its units i + grid, ... share an XCD); 0 if
+// unknown.
+static int persistent_grid() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n >= 8 ? n / 8 * 8 : -1;
+  }
+  return cus[dev] > 0 ? cus[dev] : 0;
+}
+
 template <class T, int D, bool C, bool R, bool P, int PG>
 static hipError_t launch_mfma(const FwdArgs& a) {
   using G = Geo<D>;
@@ -1031,7 +1087,14 @@ static hipError_t launch_mfma(const FwdArgs& a) {
   if (attr != hipSuccess) return attr;
   const int bs = PG ? a.block_size : 1;
   const int shift = (PG && (bs & (bs - 1)) == 0) ? __builtin_ctz((unsigned)bs) : -1;
-  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P, PG>), dim3((unsigned)total), dim3(kThreads), lds,
+  // The dense non-causal form runs persistent (one workgroup per compute unit)
+  // when there are at least two units per compute unit.
+  long long grid = total;
+  if (!C && !R && !P && PG == 0) {
+    const int cus = persistent_grid();
+    if (cus > 0 && total >= 2LL * cus) grid = cus;
+  }
+  hipLaunchKernelGGL((fa_fwd_mfma<T, D, C, R, P, PG>), dim3((unsigned)grid), dim3(kThreads), lds,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (uint16_t*)a.o, a.o_f32, a.lse, a.seq_lens,
                      a.heads_q, a.heads_q / a.heads_kv, a.n, a.m, a.key_begin, a.key_end,
