@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace fa {
 
 struct FwdArgs {
@@ -102,5 +104,22 @@ hipError_t launch_decode(const DecodeArgs& a);
 // scratch array that fa_paged_decode_noalloc uses as its workspace (looked up
 // once per device).
 hipError_t decode_scratch(void** ptr);
+
+// Compute units of the current device, rounded down to a multiple of the 8
+// XCDs (so that workgroup i and its units i + grid, ... share an XCD); 0 if
+// unknown.
+inline int persistent_grid() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n >= 8 ? n / 8 * 8 : -1;
+  }
+  return cus[dev] > 0 ? cus[dev] : 0;
+}
 
 }  // namespace fa

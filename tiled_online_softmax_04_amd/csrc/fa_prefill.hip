@@ -29,8 +29,6 @@
 // "hot" data (scores of several hundred).  Scores, the running max and the
 // shifted exponent are float64; so are the weights and the accumulator.
 
-#include <mutex>
-
 #include "fa_common.h"
 #include "fa_launch.h"
 #include "fa_lds.h"
@@ -1054,23 +1052,6 @@ __global__ __launch_bounds__(256) void fa_fwd_f32(
 // fill the 160 KB of LDS at d = 128).
 constexpr int kMaxPagedBlocks = 16384;
 constexpr int kMaxPipelinedPagedBlocks = 8192;
-
-// Compute units of the current device, rounded down to a multiple of the 8
-// XCDs (so that workgroup i and its units i + grid, ... share an XCD); 0 if
-// unknown.
-static int persistent_grid() {
-  static std::mutex mu;
-  static int cus[64] = {};
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    cus[dev] = n >= 8 ? n / 8 * 8 : -1;
-  }
-  return cus[dev] > 0 ? cus[dev] : 0;
-}
 
 template <class T, int D, bool C, bool R, bool P, int PG>
 static hipError_t launch_mfma(const FwdArgs& a) {
