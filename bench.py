@@ -256,7 +256,7 @@ def time_fp8(fa, gen, x, iters: int):
     import torch
     if iters <= 0:
         return None
-    w = gen.WORKLOADS["cfg2_fp8"]
+    w = gen.WORKLOADS["fp8_b4_2048"]
     q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
     out = torch.empty((w.B, w.Hq, w.n, w.dv), dtype=torch.bfloat16, device=q8.device)
     ms = timed_calls(lambda: fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"],
@@ -268,7 +268,7 @@ def time_fp8(fa, gen, x, iters: int):
                         "V stored as FP8 E4M3 with per-tensor descales, bf16 output",
             "tflops": round(tflops, 2), **st,
             "roofline": roofline(tflops, PEAK_FP8_TFLOPS, "TFLOP/s", "mfma",
-                                 read_traffic("fa_fwd_fp8_cfg2_traffic.txt", FP8_SOURCES),
+                                 read_traffic("fa_fwd_fp8_2048_traffic.txt", FP8_SOURCES),
                                  "fa_fwd_fp8<128,false,false,2> (non-causal, no padding, "
                                  "bf16 out)")}
 
@@ -395,19 +395,19 @@ def cpu_baselines(gen, budget_s: float, drawn: dict):
     W = gen.WORKLOADS
     per = {}
     share = budget_s / 6.0
-    head = oracle_prefill_sample(W["cfg2"], drawn["cfg2"], 2 * share)
-    per["cfg2"] = head
-    for name in ("cfg1", "cfg1_hot"):
+    head = oracle_prefill_sample(W["bf16_b4_2048"], drawn["bf16_b4_2048"], 2 * share)
+    per["bf16_b4_2048"] = head
+    for name in ("f32_256", "f32_256_hot"):
         per[name] = oracle_prefill_sample(W[name], gen.make_prefill(W[name]), 0.5 * share,
                                           rows=256)
-    for name in ("cfg3", "cfg3_ragged", "cfg5"):
+    for name in ("bf16_causal_8192", "bf16_ragged_b8_8192", "f16_hot_causal_16384"):
         per[name] = oracle_prefill_sample(W[name], drawn[name], share)
-    per["cfg4"] = oracle_decode_sample(W["cfg4"], drawn["cfg4"], share)
+    per["decode_64seq"] = oracle_decode_sample(W["decode_64seq"], drawn["decode_64seq"], share)
     return {"value": head["value"], "unit": "TFLOP/s", "cores": int(min(blas_threads(),
                                                                         len(os.sched_getaffinity(0)))),
             "kind": "oracle", "sample": "headline workload: " + head["sample"],
             "numpy": np.__version__, "host_cores": len(os.sched_getaffinity(0)),
-            "configs": per}
+            "workloads": per}
 
 
 def main():
@@ -444,21 +444,21 @@ def main():
     # every input is drawn before the first GPU call, so that no host work
     # leaves the GPU idle between the legs and the timed steps
     it = args.leg_iters
-    drawn = {"cfg2": gen.make_prefill(gen.WORKLOADS["cfg2"]),
-             "cfg4": gen.make_decode(gen.WORKLOADS["cfg4"])}
+    drawn = {"bf16_b4_2048": gen.make_prefill(gen.WORKLOADS["bf16_b4_2048"]),
+             "decode_64seq": gen.make_decode(gen.WORKLOADS["decode_64seq"])}
     if it > 0 or args.cpu_budget > 0:
-        for name in ("cfg3_ragged", "cfg3", "cfg5"):
+        for name in ("bf16_ragged_b8_8192", "bf16_causal_8192", "f16_hot_causal_16384"):
             drawn[name] = gen.make_prefill(gen.WORKLOADS[name])
     if it > 0:
-        drawn["cfg2_fp8"] = gen.make_prefill(gen.WORKLOADS["cfg2_fp8"])
+        drawn["fp8_b4_2048"] = gen.make_prefill(gen.WORKLOADS["fp8_b4_2048"])
 
-    wp = gen.WORKLOADS["cfg2"]
-    xp = drawn["cfg2"]
+    wp = gen.WORKLOADS["bf16_b4_2048"]
+    xp = drawn["bf16_b4_2048"]
     q, k, v = (to_dev(xp[n], wp.dtype, dev) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
 
-    wd = gen.WORKLOADS["cfg4"]
-    xd = drawn["cfg4"]
+    wd = gen.WORKLOADS["decode_64seq"]
+    xd = drawn["decode_64seq"]
     dq = to_dev(xd["q"], wd.dtype, dev)
     kc, vc = to_dev(xd["k_cache"], wd.dtype, dev), to_dev(xd["v_cache"], wd.dtype, dev)
     bt = torch.from_numpy(xd["block_table"]).to(dev)
@@ -494,21 +494,21 @@ def main():
     mem = peak_memory(fa) if args.peak_memory else None
     if it > 0:
         legs["ragged"] = prefill_leg(
-            fa, gen, "cfg3_ragged", drawn["cfg3_ragged"], max(10, it // 2), 10, dev,
+            fa, gen, "bf16_ragged_b8_8192", drawn["bf16_ragged_b8_8192"], max(10, it // 2), 10, dev,
             "causal prefill bf16, left-padded ragged batch B=8 H=32 N=8192 d=dv=128, lengths "
             "U[1024, 8192] (seed 3)")
-        causal = prefill_leg(fa, gen, "cfg3", drawn["cfg3"], it, 20, dev,
+        causal = prefill_leg(fa, gen, "bf16_causal_8192", drawn["bf16_causal_8192"], it, 20, dev,
                              "causal prefill bf16 B=1 H=32 n=m=8192 d=dv=128")
-        causal["dense_twin"] = time_dense_twin(fa, gen, gen.WORKLOADS["cfg3"], drawn["cfg3"], it,
+        causal["dense_twin"] = time_dense_twin(fa, gen, gen.WORKLOADS["bf16_causal_8192"], drawn["bf16_causal_8192"], it,
                                                10, dev)
         causal["time_ratio"] = round(causal["mean_ms"] / causal["dense_twin"]["mean_ms"], 4)
         legs["causal"] = causal
         legs["hot_fp16_16384"] = prefill_leg(
-            fa, gen, "cfg5", drawn["cfg5"], it, 10, dev,
+            fa, gen, "f16_hot_causal_16384", drawn["f16_hot_causal_16384"], it, 10, dev,
             "causal prefill fp16 B=1 H=16 n=m=16384 d=dv=128, Q and K drawn x10 (scores up to "
             "~300)")
         legs["paged_prefill"] = time_paged_prefill(fa, gen, wd, kc, vc, bt, sl, xd["seq_lens"], it)
-        legs["fp8"] = time_fp8(fa, gen, drawn["cfg2_fp8"], it)
+        legs["fp8"] = time_fp8(fa, gen, drawn["fp8_b4_2048"], it)
         legs["key_split"] = time_key_split(fa, gen, q, k, v, wp, it)
 
     # the headline: warmup steps, then exactly `steps` timed steps
@@ -528,8 +528,8 @@ def main():
     pre_tflops = flops / (pre["mean_ms"] * 1e-3) / 1e12
     dec_gbps = dbytes / (dec["mean_ms"] * 1e-3) / 1e9
 
-    traffic = read_traffic("fa_fwd_mfma_bf16_cfg2_traffic.txt", PREFILL_SOURCES)
-    dec_traffic = read_traffic("fa_decode_cfg4_traffic.txt", DECODE_SOURCES)
+    traffic = read_traffic("fa_fwd_mfma_bf16_2048_traffic.txt", PREFILL_SOURCES)
+    dec_traffic = read_traffic("fa_decode_64seq_traffic.txt", DECODE_SOURCES)
 
     baseline = cpu_baselines(gen, args.cpu_budget, drawn) if args.cpu_budget > 0 else None
 

@@ -171,14 +171,14 @@ def test_fp8_full_size_whole_output():
     form) and the rms error of the whole output within twice the predicted
     spread; on sampled rows, the per-row bound as well."""
     import torch
-    w = gen.WORKLOADS["cfg2_fp8"]
-    say("[fp8] cfg2_fp8 full size, every output")
+    w = gen.WORKLOADS["fp8_b4_2048"]
+    say("[fp8] fp8_b4_2048 full size, every output")
     x = gen.make_prefill(w)
     q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
     o = fa.fwd_fp8(q8, k8, v8, x["q_descale"], x["k_descale"], x["v_descale"], scale=w.scale)
     torch.cuda.synchronize()
     got_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
-    assert_whole_bound(x, w, got_bits, False, "cfg2_fp8")
+    assert_whole_bound(x, w, got_bits, False, "fp8_b4_2048")
     rng = np.random.default_rng(13)
     samples = [(0, 0), (w.B - 1, w.Hq - 1)] + \
         [(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(6)]
@@ -190,7 +190,7 @@ def test_fp8_full_size_whole_output():
         v = oracle.dequantize(x["v"][b, h], x["v_descale"])
         ref, B_, sig = fp8_bound.row_bounds(q, rows, k, v, w.scale)
         got = gen.bf16_bits_to_f64(got_bits[b, h, rows])
-        fp8_bound.check(got, ref, B_, sig, f"cfg2_fp8 b={b} h={h} rows={rows.tolist()}", say)
+        fp8_bound.check(got, ref, B_, sig, f"fp8_b4_2048 b={b} h={h} rows={rows.tolist()}", say)
 
 
 def test_fp8_causal_8k_whole_output_and_deterministic():
@@ -201,7 +201,7 @@ def test_fp8_causal_8k_whole_output_and_deterministic():
     V's first row up to the output rounding, and two calls bitwise equal."""
     import dataclasses
     import torch
-    w = dataclasses.replace(gen.WORKLOADS["cfg3"], dtype="fp8", name="cfg3_fp8")
+    w = dataclasses.replace(gen.WORKLOADS["bf16_causal_8192"], dtype="fp8", name="fp8_causal_8192")
     say("[fp8] causal 8192 x 32 heads")
     x = gen.make_prefill(w)
     q8, k8, v8 = (torch.from_numpy(x[t]).cuda() for t in ("q", "k", "v"))
@@ -212,7 +212,7 @@ def test_fp8_causal_8k_whole_output_and_deterministic():
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "not deterministic"
     assert bool(torch.isfinite(o.float()).all())
     assert_whole_bound(x, w, o.view(torch.int16).cpu().numpy().view(np.uint16), True,
-                       "cfg3_fp8 causal 8192")
+                       "fp8_causal_8192 causal 8192")
     rng = np.random.default_rng(17)
     for h in (0, 13, w.Hq - 1):
         rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 4095, w.n - 1],
@@ -222,6 +222,6 @@ def test_fp8_causal_8k_whole_output_and_deterministic():
         v = oracle.dequantize(x["v"][0, h], x["v_descale"])
         ref, B_, sig = fp8_bound.row_bounds(q, rows, k, v, w.scale, causal=True)
         got = to_f64(o[0, h, torch.from_numpy(rows).cuda()], "bf16")
-        fp8_bound.check(got, ref, B_, sig, f"cfg3_fp8 h={h} rows={rows.tolist()}", say)
+        fp8_bound.check(got, ref, B_, sig, f"fp8_causal_8192 h={h} rows={rows.tolist()}", say)
         # row 0 attends key 0 only: O = V[0] up to the bf16 output
         assert np.all(np.abs(got[0] - v[0]) <= 2.0 ** -8 * np.abs(v[0]))

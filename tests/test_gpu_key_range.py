@@ -162,8 +162,8 @@ def test_full_size_key_split_whole_output():
     attention_range, and every element of the merged output against the
     definition; the merged result also against fa_fwd."""
     import torch
-    w = gen.WORKLOADS["cfg2"]
-    say("[key-range] cfg2 in four key ranges")
+    w = gen.WORKLOADS["bf16_b4_2048"]
+    say("[key-range] bf16_b4_2048 in four key ranges")
     x = gen.make_prefill(w)
     q, k, v, _ = dev_inputs(x, w.dtype)
     bounds = [0, 512, 1024, 1536, 2048]
@@ -200,8 +200,8 @@ def test_full_size_key_split_whole_output():
         return piece_errs, lse_ratio, merged
 
     res = pooled(one, [(b, h) for b in range(w.B) for h in range(w.Hq)])
-    assert_whole([p for r in res for p in r[0]], w.dtype, "cfg2 key pieces (fp32 o)")
+    assert_whole([p for r in res for p in r[0]], w.dtype, "bf16_b4_2048 key pieces (fp32 o)")
     worst = max(r[1] for r in res)
-    say(f"  cfg2 key pieces: worst lse error / bar = {worst:.3f}")
+    say(f"  bf16_b4_2048 key pieces: worst lse error / bar = {worst:.3f}")
     assert worst <= 1.0
-    assert_whole([r[2] for r in res], w.dtype, "cfg2 key split, merged")
+    assert_whole([r[2] for r in res], w.dtype, "bf16_b4_2048 key split, merged")

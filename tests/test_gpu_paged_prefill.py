@@ -73,7 +73,7 @@ def test_paged_prefill_small(case):
 
 def test_chunk_of_one_is_the_decode():
     import torch
-    w = gen.WORKLOADS["cfg4"]
+    w = gen.WORKLOADS["decode_64seq"]
     w = dataclasses.replace(w, num_seqs=8, len_lo=100, len_hi=3000, max_blocks_per_seq=200)
     x = gen.make_paged_chunk(w, 1)
     q = to_dev(x["q"], w.dtype)
@@ -92,9 +92,9 @@ def test_full_size_chunk_whole_output():
     the launch the benchmark times: every output element against the oracle,
     one (sequence, KV head) at a time through the block table."""
     import torch
-    w = gen.WORKLOADS["cfg4"]
+    w = gen.WORKLOADS["decode_64seq"]
     n = 512
-    say("[paged prefill] cfg4 cache, 512-token chunks")
+    say("[paged prefill] decode_64seq cache, 512-token chunks")
     x = gen.make_paged_chunk(w, n)
     o = run(x, w.dtype, w.block_size, w.scale, True)
     got_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -116,4 +116,4 @@ def test_full_size_chunk_whole_output():
         return parts
 
     res = pooled(one, [(s, g) for s in range(w.num_seqs) for g in range(w.Hkv)])
-    assert_whole([p for r in res for p in r], w.dtype, "cfg4 cache, 512-token chunks")
+    assert_whole([p for r in res for p in r], w.dtype, "decode_64seq cache, 512-token chunks")

@@ -100,8 +100,8 @@ def test_prefill_many_heads_ragged_keys(case):
         assert_parity(got[b:b + 1, h:h + 1], ref, dtype, f"{name} b={b} h={h}")
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg1_hot"])
-def test_cfg1_fp32(name):
+@pytest.mark.parametrize("name", ["f32_256", "f32_256_hot"])
+def test_f32_256_workloads(name):
     w = gen.WORKLOADS[name]
     say(f"[prefill] {name}")
     x = gen.make_prefill(w)
@@ -162,7 +162,7 @@ def whole_output_errors(x, w, got_bits):
     return (max(r[0] for r in res), sum(r[1] for r in res), sum(r[2] for r in res))
 
 
-@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg3_ragged", "cfg5"])
+@pytest.mark.parametrize("name", ["bf16_b4_2048", "bf16_causal_8192", "bf16_ragged_b8_8192", "f16_hot_causal_16384"])
 def test_full_size_whole_output(name):
     """The full workloads (bf16 2048 x 128 heads; causal 8192; the left-padded
     ragged causal batch 8 x 8192; fp16 hot causal 16384) in the launch the
@@ -298,15 +298,15 @@ def test_decode_offset_values_absolute_bar(dtype, offset):
     assert mean <= floor + 1e-3, f"mean abs {mean:.3e} > {floor:.3e} + 1e-3"
 
 
-def test_decode_cfg4_full():
-    w = gen.WORKLOADS["cfg4"]
-    say("[decode] cfg4 generating")
+def test_decode_64seq_full():
+    w = gen.WORKLOADS["decode_64seq"]
+    say("[decode] decode_64seq generating")
     x = gen.make_decode(w)
-    say("[decode] cfg4 running")
+    say("[decode] decode_64seq running")
     got = to_f64(run_decode(x, w.dtype, w.block_size, w.scale), w.dtype)
-    say("[decode] cfg4 oracle")
+    say("[decode] decode_64seq oracle")
     ref = decode_oracle(x, w.dtype, w.block_size, w.scale)
-    assert_parity(got, ref, w.dtype, "cfg4 (all outputs)")
+    assert_parity(got, ref, w.dtype, "decode_64seq (all outputs)")
 
 
 def test_decode_block_placement_invariance_and_determinism():

@@ -48,7 +48,7 @@ def test_prefill_deterministic_and_shaped():
 def test_scale_is_float32_rounded():
     """A float64 1/sqrt(d) silently promotes fp32 arithmetic (10100.com section
     4); the workloads carry the float32 value the kernel receives."""
-    w = gen.WORKLOADS["cfg2"]
+    w = gen.WORKLOADS["bf16_b4_2048"]
     assert w.scale == float(np.float32(1 / math.sqrt(128)))
 
 
@@ -69,17 +69,17 @@ def test_decode_table_is_a_permutation_with_poisoned_tails():
 
 
 def test_algorithmic_counts():
-    assert gen.prefill_flops(gen.WORKLOADS["cfg2"]) == 4 * 4 * 32 * 2048 * 2048 * 128
-    assert abs(gen.prefill_flops(gen.WORKLOADS["cfg2"]) - 2.749e11) < 1e9
-    assert abs(gen.prefill_flops(gen.WORKLOADS["cfg3"]) - 5.498e11) < 1e9
-    assert abs(gen.prefill_flops(gen.WORKLOADS["cfg5"]) - 1.0996e12) < 1e9
-    w = gen.WORKLOADS["cfg4"]
+    assert gen.prefill_flops(gen.WORKLOADS["bf16_b4_2048"]) == 4 * 4 * 32 * 2048 * 2048 * 128
+    assert abs(gen.prefill_flops(gen.WORKLOADS["bf16_b4_2048"]) - 2.749e11) < 1e9
+    assert abs(gen.prefill_flops(gen.WORKLOADS["bf16_causal_8192"]) - 5.498e11) < 1e9
+    assert abs(gen.prefill_flops(gen.WORKLOADS["f16_hot_causal_16384"]) - 1.0996e12) < 1e9
+    w = gen.WORKLOADS["decode_64seq"]
     L = np.full(64, 16 * 10)
     assert gen.decode_bytes(w, L) == (64 * 160 * 8 * 256 * 2 + 64 * 32 * 256 * 2
                                       + 64 * 10 * 4 + 64 * 4)
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg1_hot"])
+@pytest.mark.parametrize("name", ["f32_256", "f32_256_hot"])
 def test_small_workload_values(name):
     w = gen.WORKLOADS[name]
     x = gen.make_prefill(w)

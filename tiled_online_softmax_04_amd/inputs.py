@@ -157,16 +157,16 @@ class Decode:
 
 # The five workloads (sizes as the benchmark spec gives them).
 WORKLOADS = {
-    "cfg1": Prefill("cfg1", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1),
-    "cfg1_hot": Prefill("cfg1_hot", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1, hot=10.0),
-    "cfg2": Prefill("cfg2", "bf16", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
-    "cfg3": Prefill("cfg3", "bf16", 1, 32, 32, 8192, 8192, 128, 128, True, seed=3),
-    "cfg3_ragged": Prefill("cfg3_ragged", "bf16", 8, 32, 32, 8192, 8192, 128, 128, True,
+    "f32_256": Prefill("f32_256", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1),
+    "f32_256_hot": Prefill("f32_256_hot", "f32", 1, 1, 1, 256, 256, 64, 64, False, seed=1, hot=10.0),
+    "bf16_b4_2048": Prefill("bf16_b4_2048", "bf16", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
+    "bf16_causal_8192": Prefill("bf16_causal_8192", "bf16", 1, 32, 32, 8192, 8192, 128, 128, True, seed=3),
+    "bf16_ragged_b8_8192": Prefill("bf16_ragged_b8_8192", "bf16", 8, 32, 32, 8192, 8192, 128, 128, True,
                            seed=3, ragged=(1024, 8192)),
-    "cfg4": Decode("cfg4", "bf16", 64, 32, 8, 128, 128, 16, 512, 8192, 512, seed=4),
-    "cfg5": Prefill("cfg5", "f16", 1, 16, 16, 16384, 16384, 128, 128, True, seed=5, hot=10.0),
+    "decode_64seq": Decode("decode_64seq", "bf16", 64, 32, 8, 128, 128, 16, 512, 8192, 512, seed=4),
+    "f16_hot_causal_16384": Prefill("f16_hot_causal_16384", "f16", 1, 16, 16, 16384, 16384, 128, 128, True, seed=5, hot=10.0),
     # the bf16 2048-token prefill with FP8 (E4M3) storage
-    "cfg2_fp8": Prefill("cfg2_fp8", "fp8", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
+    "fp8_b4_2048": Prefill("fp8_b4_2048", "fp8", 4, 32, 32, 2048, 2048, 128, 128, False, seed=2),
 }
 
 
