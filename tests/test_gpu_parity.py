@@ -80,6 +80,42 @@ WIDE = [
 ]
 
 
+PERSISTENT = [
+    # name, dtype, B, Hq, Hkv, n, m, d: dense non-causal calls of 540-600 units
+    # (query tiles of 256 rows), more than two per compute unit, so one
+    # workgroup per compute unit walks two or three units each; n is not a
+    # multiple of 256, so every head's last unit has rows past n.
+    ("persistent_bf16_d64_600_units", "bf16", 1, 200, 40, 600, 600, 64),
+    ("persistent_f16_d128_540_units", "f16", 2, 90, 30, 700, 650, 128),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=[c[0] for c in PERSISTENT])
+def test_prefill_persistent_launch_every_head(case):
+    """The dense form that keeps each unit's output rows in registers until
+    the next unit's copies are out: every output element of every head
+    against the oracle, and two calls bitwise equal."""
+    name, dtype, B, Hq, Hkv, n, m, d = case
+    say(f"[prefill] {name}")
+    x = gen.make_prefill_custom(dtype, B, Hq, Hkv, n, m, d, d,
+                                seed=zlib.crc32(name.encode()) % 1000)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    import torch
+    raw1 = run_prefill(x, dtype, False, scale, None)
+    raw2 = run_prefill(x, dtype, False, scale, None)
+    assert torch.equal(raw1, raw2), "two calls differ"
+    got = to_f64(raw1, dtype)
+    q, k, v = f64_inputs(x, dtype)
+    g = Hq // Hkv
+    ref = np.empty_like(got)
+    for b in range(B):
+        for h in range(Hq):
+            ref[b:b + 1, h:h + 1] = oracle.attention(
+                q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1],
+                v[b:b + 1, h // g:h // g + 1], scale, False)
+    assert_parity(got, ref, dtype, f"{name}, every output")
+
+
 @pytest.mark.parametrize("case", WIDE, ids=[c[0] for c in WIDE])
 def test_prefill_many_heads_ragged_keys(case):
     """Non-causal calls of 512 workgroups whose key ranges end inside a tile
