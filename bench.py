@@ -156,7 +156,7 @@ def prefill_leg(fa, gen, name: str, x, iters: int, warm: int, dev, label: str):
            "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
                                 PREFILL_KERNEL.format(c=str(w.causal).lower(),
                                                       r=str(x["seq_lens"] is not None).lower(),
-                                                      p="false").replace("BF16", w.dtype.upper()))}
+                                                      p="0").replace("BF16", w.dtype.upper()))}
     if x["seq_lens"] is not None:
         res["seq_lens"] = [int(a) for a in x["seq_lens"]]
     del q, k, v, out
@@ -178,7 +178,7 @@ def time_dense_twin(fa, gen, w, x, iters, warm, dev):
     torch.cuda.empty_cache()
     return {"tflops": round(tflops, 2), **st,
             "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
-                                 PREFILL_KERNEL.format(c="false", r="false", p="false"))}
+                                 PREFILL_KERNEL.format(c="false", r="false", p="0"))}
 
 
 def time_key_split(fa, gen, q, k, v, wp, iters: int):
@@ -222,7 +222,7 @@ def time_key_split(fa, gen, q, k, v, wp, iters: int):
             "tflops_total": round(flops / ((part["mean_ms"] + merge["mean_ms"]) * 1e-3) / 1e12, 2),
             "pieces": {**part, "tflops": round(pieces_tflops, 2),
                        "roofline": roofline(pieces_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma",
-                                            None, "fa_fwd_mfma<BF16,128,false,false,true,false>")},
+                                            None, "fa_fwd_mfma<BF16,128,false,false,true,0>")},
             "merge": {**merge, "gbps": round(merge_gbps, 1), "bytes": merge_bytes,
                       "roofline": roofline(merge_gbps, PEAK_HBM_GBPS, "GB/s", "hbm", None,
                                            "fa_merge_lse<2>")}}
@@ -247,7 +247,7 @@ def time_paged_prefill(fa, gen, wd, kc, vc, bt, sl, seq_lens, iters: int, n: int
                         "random placement)",
             "tflops": round(tflops, 2), "flop": flops, **st,
             "roofline": roofline(tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", None,
-                                 "fa_fwd_mfma<BF16,128,true,false,false,true>")}
+                                 "fa_fwd_mfma<BF16,128,true,false,false,1>")}
 
 
 def time_fp8(fa, gen, x, iters: int):
@@ -552,7 +552,7 @@ def main():
                    "prefill_flop": flops, "decode_bytes": dbytes, "seed_prefill": wp.seed,
                    "seed_decode": wd.seed},
         "roofline": {**roofline(pre_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma", traffic,
-                                "fa_fwd_mfma<BF16,128,false,false,false,false> (non-causal, no "
+                                "fa_fwd_mfma<BF16,128,false,false,false,0> (non-causal, no "
                                 "padding, full key range, contiguous)"),
                      "avg_launch_ms": pre["mean_ms"]},
         "prefill_times": {**pre, "tflops_at_median": round(flops / (pre["median_ms"] * 1e-3)

@@ -27,6 +27,10 @@ __device__ __forceinline__ int kappa(int r) {
   return r ^ ((((r >> 2) ^ (r >> 3)) & 1) * 0xC);
 }
 
+// Fourth word of the raw buffer descriptors here: data format 32 bits (bits
+// 15-18 = 4), no swizzle, no index stride, everything else zero.
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
 // Raw buffer descriptor over [base, base + bytes) as four words, for
 // dma16_untracked: base address, no stride, `bytes` of range.  Loads at
 // offsets outside the range (including "negative" offsets, which wrap past
@@ -35,7 +39,7 @@ __device__ __forceinline__ u32x4 make_rsrc_words(const void* base, uint32_t byte
   const uint64_t b = (uint64_t)(uintptr_t)base;
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu),
-               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3};
 }
 
 // 16 bytes per lane straight from a buffer into LDS: the wave's 64 lanes fill

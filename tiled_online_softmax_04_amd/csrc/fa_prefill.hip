@@ -922,7 +922,7 @@ __global__ __launch_bounds__(kThreads, FA_PREFILL_WAVES_PER_EU) void fa_fwd_mfma
       // Held until the next unit's copies are out (or the end of the launch).
       RS::read(ob, lane, o_pend);
       o_pend_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          O + q_base + (size_t)r0 * D, 0, max(n - r0, 0) * (D * 2), 0x00020000);
+          O + q_base + (size_t)r0 * D, 0, max(n - r0, 0) * (D * 2), (int)kRsrcWord3);
       have_pend = true;
     } else {
       RS::store(ob, lane, reinterpret_cast<char*>(O + q_base + (size_t)r0 * D), (size_t)D * 2,
