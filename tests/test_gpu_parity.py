@@ -147,12 +147,17 @@ def test_f32_256_workloads(name):
     assert_parity(to_f64(o, "f32"), ref, "f32", name)
 
 
-def test_empty_key_set_gives_zero():
+@pytest.mark.parametrize("B,H,n,d", [(1, 2, 40, 128), (2, 130, 600, 64)],
+                         ids=["one_unit", "persistent_780_units"])
+def test_empty_key_set_gives_zero(B, H, n, d):
+    """No keys at all: every output row is 0 (the second shape has enough
+    query tiles for the persistent dense form)."""
     import torch
-    say("[prefill] no keys")
-    q = torch.randn(1, 2, 40, 128, device="cuda").to(torch.bfloat16)
-    k = torch.zeros(1, 2, 0, 128, device="cuda", dtype=torch.bfloat16)
-    o = fa.fwd(q, k, k)
+    say(f"[prefill] no keys, B={B} H={H} n={n} d={d}")
+    q = torch.randn(B, H, n, d, device="cuda").to(torch.bfloat16)
+    k = torch.zeros(B, H, 0, d, device="cuda", dtype=torch.bfloat16)
+    o = torch.full_like(q, float("nan"))
+    fa.fwd(q, k, k, out=o)
     torch.cuda.synchronize()
     assert torch.all(o == 0)
 
