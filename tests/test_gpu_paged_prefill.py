@@ -71,6 +71,36 @@ def test_paged_prefill_small(case):
             assert np.all(got[s, :, :n - L] == 0), "rows before the sequence must be 0"
 
 
+def _random_cases():
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(16):
+        dtype = ["bf16", "f16"][int(rng.integers(2))]
+        d = [64, 128][int(rng.integers(2))]
+        S = int(rng.integers(1, 5))
+        Hkv = [1, 2, 4][int(rng.integers(3))]
+        Hq = Hkv * [1, 2, 4][int(rng.integers(3))]
+        bs = [1, 2, 8, 16, 32, 64, 128, 5, 12, 48][int(rng.integers(10))]
+        lens = [int(x) for x in rng.integers(0, 900, size=S)]
+        maxb = max(1, (max(lens) + bs - 1) // bs + int(rng.integers(0, 3)))
+        n = int(rng.integers(1, 300))
+        causal = bool(rng.integers(2))
+        out.append((f"r{i:02d}_{dtype}_d{d}_S{S}_H{Hq}x{Hkv}_bs{bs}_n{n}{'_causal' if causal else ''}",
+                    dtype, S, Hq, Hkv, d, bs, lens, maxb, n, causal))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_paged_prefill_random(case):
+    """Seeded random shapes (block sizes powers of two and not, empty and
+    short sequences, chunks longer than their sequence): every output element
+    against the oracle, rows before a sequence's first token exactly 0."""
+    test_paged_prefill_small(case)
+
+
 def test_chunk_of_one_is_the_decode():
     import torch
     w = gen.WORKLOADS["decode_64seq"]
