@@ -287,6 +287,36 @@ def test_decode_small(case):
             assert np.all(got[s] == 0)
 
 
+def _random_decode_cases():
+    rng = np.random.default_rng(20261205)
+    out = []
+    for i in range(16):
+        dtype = ["bf16", "f16"][int(rng.integers(2))]
+        d = [64, 128][int(rng.integers(2))]
+        S = int(rng.integers(1, 40))
+        Hkv = [1, 2, 4, 8][int(rng.integers(4))]
+        Hq = Hkv * [1, 2, 4, 8][int(rng.integers(4))]
+        bs = [1, 4, 16, 32, 64, 7, 24][int(rng.integers(7))]
+        hi = [64, 1000, 6000][int(rng.integers(3))]
+        lens = [int(x) for x in rng.integers(0, hi + 1, size=S)]
+        maxb = max(1, (max(lens) + bs - 1) // bs + int(rng.integers(0, 3)))
+        out.append((f"r{i:02d}_{dtype}_d{d}_S{S}_H{Hq}x{Hkv}_bs{bs}_upto{hi}",
+                    dtype, S, Hq, Hkv, d, bs, lens, maxb))
+    return out
+
+
+DEC_RANDOM = _random_decode_cases()
+
+
+@pytest.mark.parametrize("case", DEC_RANDOM, ids=[c[0] for c in DEC_RANDOM])
+def test_decode_random(case):
+    """Seeded random decode batches (1-39 sequences, lengths 0 up to 6000,
+    block sizes powers of two and not, 1-8 query heads per KV head, so that
+    the split size halves for small batches): every output against the
+    oracle, empty sequences exactly 0."""
+    test_decode_small(case)
+
+
 @pytest.mark.parametrize("dtype,factor", [("f16", 2.0e4), ("bf16", 1.0e30)])
 def test_decode_large_values(dtype, factor):
     """Values near the top of the input type's range: each split's output is a
