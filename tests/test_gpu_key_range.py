@@ -118,6 +118,60 @@ def test_merge_reproduces_full_pass(case):
             assert np.all(got[b, :, :p] == 0)
 
 
+def _random_cases():
+    rng = np.random.default_rng(20261206)
+    out = []
+    for i in range(12):
+        dtype = ["bf16", "f16"][int(rng.integers(2))]
+        d = [64, 128][int(rng.integers(2))]
+        B = int(rng.integers(1, 4))
+        Hkv = [1, 2, 4][int(rng.integers(3))]
+        Hq = Hkv * [1, 2, 4][int(rng.integers(3))]
+        causal = bool(rng.integers(2))
+        n = int(rng.integers(1, 700))
+        ragged = rng.random() < 0.3
+        m = n if (causal or ragged) else int(rng.integers(1, 700))
+        lens = [int(x) for x in rng.integers(0, n + 1, size=B)] if ragged else None
+        cuts = np.sort(rng.integers(0, m + 1, size=int(rng.integers(0, 4)))).tolist()
+        bounds = [0, *cuts, m]
+        out.append((f"r{i:02d}_{dtype}_d{d}_B{B}_H{Hq}x{Hkv}_n{n}_m{m}"
+                    f"{'_causal' if causal else ''}{'_pad' if ragged else ''}_{len(bounds) - 1}pieces",
+                    dtype, B, Hq, Hkv, n, m, d, causal, 1.0, lens,
+                    list(zip(bounds[:-1], bounds[1:]))))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_partition(case):
+    """Seeded random shapes, each cut into 1-4 key ranges (empty ones
+    included): every piece's o and lse against the oracle's attention_range,
+    and their merge against the definition."""
+    import torch
+    name, dtype, causal, ranges = case[0], case[1], case[8], case[11]
+    say(f"[key-range random] {name} {ranges}")
+    x, scale = make(case)
+    q, k, v, sl = dev_inputs(x, dtype)
+    qf, kf, vf = (gen.to_f64(x[t], dtype) for t in ("q", "k", "v"))
+    pieces = []
+    for lo, hi in ranges:
+        o, lse = fa.fwd_partial(q, k, v, lo, hi, scale=scale, causal=causal, seq_lens=sl)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.attention_range(qf, kf, vf, scale, causal, x["pads"], lo, hi)
+        got_o, got_l = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+        assert_parity(got_o, ref_o, dtype, f"{name} [{lo},{hi}) o")
+        check_lse(got_l, ref_l, dtype, f"{name} [{lo},{hi})")
+        assert np.all(got_o[np.isneginf(ref_l)] == 0), "rows without keys must give o = 0"
+        pieces.append((o, lse))
+    out = fa.merge(torch.stack([p_[0] for p_ in pieces]), torch.stack([p_[1] for p_ in pieces]),
+                   out_dtype=q.dtype)
+    torch.cuda.synchronize()
+    ref = oracle.attention(qf, kf, vf, scale, causal, pads=x["pads"])
+    assert_parity(to_f64(out, dtype), ref, dtype, f"{name} merged")
+
+
 @pytest.mark.parametrize("bounds", [[0, 17, 17, 40, 64], [0, 9, 17, 17, 30, 40, 64]],
                          ids=["4pieces", "6pieces"])
 def test_merge_kernel_on_oracle_pieces(bounds):
