@@ -88,6 +88,36 @@ def test_fp8_small(case):
             assert np.all(got[b, :, :p] == 0)
 
 
+def _random_cases():
+    rng = np.random.default_rng(20261207)
+    out = []
+    for i in range(12):
+        o = ["bf16", "f16", "f32"][int(rng.integers(3))]
+        d = [64, 128][int(rng.integers(2))]
+        B = int(rng.integers(1, 4))
+        Hkv = [1, 2, 4][int(rng.integers(3))]
+        Hq = Hkv * [1, 2, 4][int(rng.integers(3))]
+        causal = bool(rng.integers(2))
+        n = int(rng.integers(1, 600))
+        ragged = rng.random() < 0.3
+        m = n if (causal or ragged) else int(rng.integers(1, 600))
+        lens = [int(x) for x in rng.integers(0, n + 1, size=B)] if ragged else None
+        out.append((f"r{i:02d}_{o}_d{d}_B{B}_H{Hq}x{Hkv}_n{n}_m{m}"
+                    f"{'_causal' if causal else ''}{'_pad' if ragged else ''}",
+                    o, B, Hq, Hkv, n, m, d, causal, 1.0, lens))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_fp8_random(case):
+    """Seeded random shapes (all three output types, GQA, n != m, causal,
+    left-padded batches): every output within the per-element bound."""
+    test_fp8_small(case)
+
+
 @pytest.mark.parametrize("causal,lens", [(False, None), (True, None), (True, [300, 77])])
 def test_fp8_equal_scores_give_means(causal, lens):
     """Q = 0: every allowed key weighs exactly 1 in E4M3, so O is the mean of V
